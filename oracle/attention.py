@@ -1,0 +1,159 @@
+"""CPU oracle for causal / key-padded scaled dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it. It shares no code with the HIP library (no kernels, headers, tables or
+helpers) and never receives a value produced by the GPU path.
+
+What it computes, and where that is defined:
+
+* Forward: eq. (1) and eqs. (4)-(6) of the CS336 Assignment 2 (systems) handout, §4.1
+  "Optimizing Attention with FlashAttention-2": ``S = scale * Q K^T``, masked entries removed,
+  row softmax ``P``, ``O = P V``.  The logsumexp ``L_i = log sum_j exp(S_ij)`` is eq. (12),
+  natural log, over the unmasked entries of row i.
+* Masking: Problem (flash_forward)(c) of the same handout builds a square causal mask from
+  query and key index vectors and pushes masked scores to a large negative value so they get
+  no weight. Here the weight of a masked entry is exactly 0 (``np.where``), which is what the
+  large negative constant achieves after ``exp`` underflows. A key-padding length ``kv``
+  additionally removes keys ``j >= kv`` for every query of that batch row.
+* Backward: the *textbook* form, eqs. (7)-(11): ``dV = P^T dO``, ``dP = dO V^T``,
+  ``dS_i = (diag(P_i) - P_i P_i^T) dP_i``, ``dQ = scale * dS K``, ``dK = scale * dS^T Q``.
+  It deliberately does not use the ``D = rowsum(O o dO)`` shortcut of eqs. (13)-(19); the
+  row dot product ``P_i . dP_i`` is taken from P and dP, so the oracle is independent of the
+  pre-pass it is used to check.  ``rowsum_p_dp`` returns that dot product as ``D_ref``.
+* Theorem 1 of "Notes on flashattention" (section Analysis / Correctness) shows the tiled
+  online-softmax forward returns exactly ``softmax(S) V``; that is why an untiled, materialised
+  reference is the right thing to compare a tiled kernel against.
+
+Everything is float64 numpy, one (batch, head) at a time, materialising the full N x N
+matrices. The only library primitive used as a step is the matrix product.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "valid_mask",
+    "head_forward",
+    "head_backward",
+    "attention_forward",
+    "attention_backward",
+    "rowsum_p_dp",
+    "rowsum_o_do",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast to float64 (exact for bf16 and fp32 inputs). Accepts numpy arrays or CPU torch tensors."""
+    if hasattr(x, "detach"):  # a CPU torch tensor: go through float32/float64 on the torch side
+        import torch
+
+        x = x.detach().to(dtype=torch.float64, device="cpu").numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def valid_mask(n: int, causal: bool, kv: int | None) -> np.ndarray:
+    """Boolean ``[n, n]`` matrix, True where query i may attend key j.
+
+    Causal (handout Problem (flash_forward)(c)): key j is masked for query i when j > i; the
+    diagonal is kept (square mask, equal query and key lengths).  Key padding: keys j >= kv are
+    masked for every query.  ``kv=None`` means no padding.
+    """
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    ok = np.ones((n, n), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if kv is not None:
+        ok &= j < kv
+    return ok
+
+
+def head_forward(q, k, v, *, causal: bool, scale: float, kv: int | None = None):
+    """One head. q, k, v: ``[N, d]``. Returns ``(O [N, d], L [N], P [N, N])`` in float64.
+
+    Eq. (4): S = scale * q k^T.  Eq. (5): row softmax over the unmasked entries (shifted by the
+    row maximum for stability; the shift cancels).  Eq. (6): O = P v.  Eq. (12): L = log of the
+    row sum of exp(S) over unmasked entries, written as m + log(sum exp(S - m)).
+    Every row must keep at least one key (kv >= 1); a fully masked row is rejected.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = q.shape[0]
+    ok = valid_mask(n, causal, kv)
+    if not ok.any(axis=1).all():
+        raise ValueError("a query row has no unmasked key (kv_len must be >= 1)")
+    s = scale * (q @ k.T)
+    m = np.where(ok, s, -np.inf).max(axis=1)
+    e = np.where(ok, np.exp(np.where(ok, s, 0.0) - m[:, None]), 0.0)
+    denom = e.sum(axis=1)
+    p = e / denom[:, None]
+    lse = m + np.log(denom)
+    o = p @ v
+    return o, lse, p
+
+
+def head_backward(q, k, v, do, *, causal: bool, scale: float, kv: int | None = None):
+    """One head. Returns ``(dQ, dK, dV, D_ref)`` in float64 via the textbook eqs. (7)-(11).
+
+    dV = P^T dO (7); dP = dO v^T (8); dS_i = P_i o dP_i - P_i (P_i . dP_i) which is eq. (9)'s
+    (diag(P_i) - P_i P_i^T) dP_i written row by row; dQ = scale dS k (10); dK = scale dS^T q (11).
+    D_ref is the row dot product P_i . dP_i taken on the way.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _, _, p = head_forward(q, k, v, causal=causal, scale=scale, kv=kv)
+    dv = p.T @ do
+    dp = do @ v.T
+    d_ref = (p * dp).sum(axis=1)
+    ds = p * dp - p * d_ref[:, None]
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv, d_ref
+
+
+def _kv_of(kv_len, b: int):
+    if kv_len is None:
+        return None
+    return int(np.asarray(kv_len).reshape(-1)[b])
+
+
+def attention_forward(q, k, v, *, causal: bool, scale: float, kv_len=None, heads=None):
+    """Batched forward over ``[B, H, N, d]``. Returns ``(O [B,H,N,d], L [B,H,N])`` float64.
+
+    ``kv_len``: per-batch key lengths ``[B]`` or None. ``heads``: optional list of ``(b, h)``
+    pairs; when given only those heads are computed and the result arrays hold NaN elsewhere.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    o = np.full((B, H, N, v.shape[-1]), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    for b, h in heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]:
+        o[b, h], lse[b, h], _ = head_forward(
+            q[b, h], k[b, h], v[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b)
+        )
+    return o, lse
+
+
+def attention_backward(q, k, v, do, *, causal: bool, scale: float, kv_len=None, heads=None):
+    """Batched backward. Returns ``(dQ, dK, dV, D_ref)`` float64 (NaN outside ``heads`` if given)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    dref = np.full((B, H, N), np.nan)
+    for b, h in heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]:
+        dq[b, h], dk[b, h], dv[b, h], dref[b, h] = head_backward(
+            q[b, h], k[b, h], v[b, h], do[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b)
+        )
+    return dq, dk, dv, dref
+
+
+def rowsum_p_dp(q, k, v, do, *, causal: bool, scale: float, kv_len=None, heads=None):
+    """``D_i = P_i . dP_i`` from the materialised P and dP (the quantity eq. (9) needs)."""
+    return attention_backward(q, k, v, do, causal=causal, scale=scale, kv_len=kv_len, heads=heads)[3]
+
+
+def rowsum_o_do(o, do):
+    """``D = rowsum(O o dO)`` (handout §4.1, "backward pass with recomputation"), float64."""
+    return (_f64(o) * _f64(do)).sum(axis=-1)
