@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark: causal attention forward + backward on one MI355X, through the C ABI.
+
+One step = the whole path over one batch: attn_fwd, then the backward's three kernels
+(attn_bwd_rowdot, attn_bwd_dkdv, attn_bwd_dq -- exactly what attn_bwd launches), on torch's
+current HIP stream, with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
+bracketed by torch.cuda.synchronize(); HIP events recorded on the same stream between the kernels
+give each kernel's average duration.  Prints one JSON line.
+
+Algorithmic FLOPs (matrix products only, 2 FLOPs per multiply-add; causal-skipped half and the
+dQ kernel's recompute of S and dP not counted):
+  npairs = sum_i (number of unmasked keys of query i)
+  forward 4*d*npairs per head (Q K^T and P V), backward 10*d*npairs per head (S, dP, dV, dK, dQ).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attention fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "gpt2-small"
+KERNELS = ("fwd", "rowdot", "dkdv", "dq")
+KERNEL_SOURCES = ("attn_device.h", "attn_fwd.hip", "attn_bwd.hip")
+
+
+def npairs(N: int, kv: int, causal: bool) -> int:
+    if not causal:
+        return N * kv
+    # sum_{i<N} min(i+1, kv)
+    m = min(N, kv)
+    return m * (m + 1) // 2 + (N - m) * kv
+
+
+def kernel_work(w, kv: int) -> dict:
+    """Algorithmic work per launch of each kernel: FLOPs for the MFMA kernels, bytes for rowdot."""
+    BH, d = w.B * w.H, w.d
+    P = npairs(w.N, kv, w.causal)
+    es = 2 if w.dtype == "bf16" else 4
+    return {
+        "fwd": ("flop", 4 * d * P * BH),
+        "rowdot": ("byte", 2 * BH * w.N * d * es + BH * w.N * 4),
+        "dkdv": ("flop", 8 * d * P * BH),   # S, dP, dV, dK
+        "dq": ("flop", 2 * d * P * BH),     # dQ (its recompute of S and dP is not credited)
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_self_attention_flashattention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("source_hash") != kernel_source_hash():
+                return None
+            k = rec.get("kernels", {}).get(kernel)
+            return None if k is None else k.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline(inputs, w, kv_list, target_s: float):
+    """Time the float64 oracle (as it stands) on a bounded sample of heads of the same workload."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle.attention as O
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        b, h = heads[done % len(heads)]
+        kv = None if kv_list is None else kv_list[b]
+        q, k, v, do = (inputs[n][b, h] for n in ("q", "k", "v", "do"))
+        O.head_forward(q, k, v, causal=w.causal, scale=w.scale, kv=kv)
+        O.head_backward(q, k, v, do, causal=w.causal, scale=w.scale, kv=kv)
+        flops += 14 * w.d * npairs(w.N, w.N if kv is None else kv, w.causal)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 64 * len(heads):
+            break
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} (batch, head) fwd+bwd passes of the {w.name} workload "
+                  f"({done / len(heads):.2f} x its {len(heads)} heads), float64 numpy, {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): attention is independent "
+              "per (batch, head), so more GPUs would only split heads; no multi-GPU run is provided.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_self_attention_flashattention_amd as attn
+    from causal_self_attention_flashattention_amd.inputs import WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[args.workload]
+    inputs = make_workload_inputs(w, args.seed)
+    kv_list = None if inputs["kv_len"] is None else inputs["kv_len"].tolist()
+    kv = w.N if kv_list is None else kv_list[0]
+    assert kv_list is None or len(set(kv_list)) == 1
+    dev = torch.device("cuda:0")
+    g = {k: (None if t is None else t.to(dev)) for k, t in inputs.items()}
+    q, k, v, do, kvd = g["q"], g["k"], g["v"], g["do"], g["kv_len"]
+    o, L = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    D = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    attn.load_library()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        attn.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_len=kvd, out=o, lse=L)
+        if ev is not None:
+            ev[1].record()
+        attn.rowdot(o, do, out=D)
+        if ev is not None:
+            ev[2].record()
+        attn.bwd_dkdv(q, k, v, do, L, D, causal=w.causal, scale=w.scale, kv_len=kvd, outs=(dk, dv))
+        if ev is not None:
+            ev[3].record()
+        attn.bwd_dq(q, k, v, do, L, D, causal=w.causal, scale=w.scale, kv_len=kvd, out=dq)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per_kernel_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                     for j, name in enumerate(KERNELS)}
+    event_ms_per_step = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
+
+    work = kernel_work(w, kv)
+    P = npairs(w.N, kv, w.causal)
+    total_flop = 14 * w.d * P * w.B * w.H
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # roofline of the dominant kernel
+    dom = max(KERNELS, key=lambda n: per_kernel_ms[n])
+    kind, amount = work[dom]
+    t = per_kernel_ms[dom] * 1e-3
+    if kind == "flop":
+        roof = {"bound": "mfma", "achieved": amount / t / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": amount / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(dom, w.name)
+    roof["kernel"] = dom
+
+    kernels = {}
+    for n in KERNELS:
+        kd, amt = work[n]
+        tt = per_kernel_ms[n] * 1e-3
+        kernels[n] = {"us": per_kernel_ms[n] * 1e3,
+                      ("TFLOP/s" if kd == "flop" else "GB/s"): amt / tt / (1e12 if kd == "flop" else 1e9)}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "kv_len": kv, "seed": w.seed if args.seed is None else args.seed,
+                   "pct_of_peak": 100.0 * value / peak, "peak_tflops": peak,
+                   "event_ms_per_step": event_ms_per_step, "kernels": kernels},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inputs, w, kv_list, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

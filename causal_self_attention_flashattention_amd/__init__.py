@@ -1,0 +1,19 @@
+"""MI355X-native tiled causal self-attention (FlashAttention-2 style), forward and backward.
+
+The computation lives in ``libattn.so`` (HIP kernels for gfx950 behind a C ABI, see
+``include/attn.h``); this package is a thin ctypes binding plus the seeded input generator.
+"""
+
+from .binding import (  # noqa: F401
+    AttnError,
+    bwd,
+    bwd_dkdv,
+    bwd_dq,
+    fwd,
+    load_library,
+    rowdot,
+    status_string,
+    supported,
+)
+
+__all__ = ["fwd", "bwd", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

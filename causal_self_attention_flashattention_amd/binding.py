@@ -1,0 +1,174 @@
+"""Thin ctypes binding over libattn's C ABI (include/attn.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP stream; every step
+of the computation runs in the library's HIP kernels.  There is no fallback: if the library is
+not built, or no GPU is present, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+_DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+# Names and C signatures of every exported entry point (kept in step with include/attn.h).
+_vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_bwd_rowdot": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_status_string": (ctypes.c_char_p, [_i]),
+    "attn_supported": (_i, [_i, _i]),
+    "attn_version": (_i, []),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so (once) and declare its signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libattn.so not found at {path}: build it with "
+            "`python -m causal_self_attention_flashattention_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise AttnError(fn, status, status_string(status))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_qkv(*ts):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if ref.dtype not in _DTYPES:
+        raise TypeError(f"dtype {ref.dtype} not supported (float32, bfloat16)")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("Q, K, V, O, dO must share shape and dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+    return ref.shape
+
+
+def _kv_tensor(kv_len, B, device):
+    if kv_len is None:
+        return None
+    if isinstance(kv_len, torch.Tensor):
+        t = kv_len
+    else:
+        t = torch.tensor([int(kv_len)] * B if isinstance(kv_len, int) else list(kv_len), dtype=torch.int32)
+    t = t.to(device=device, dtype=torch.int32).contiguous()
+    if t.numel() != B:
+        raise ValueError("kv_len must hold one length per batch row")
+    return t
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, out=None, lse=None):
+    """Attention forward. Returns ``(O, L)``: O like q, L float32 [B, H, N] (natural log)."""
+    B, H, N, d = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    kv = _kv_tensor(kv_len, B, q.device)
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)),
+                                 scale, _DTYPES[q.dtype], _ptr(kv), _stream())
+    _check("attn_fwd", st)
+    return o, L
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv_len=None, outs=None):
+    """Attention backward. Returns ``(dQ, dK, dV, D)``; D = rowsum(O o dO) float32 [B, H, N]."""
+    B, H, N, d = _check_qkv(q, k, v, o, do)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if outs is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, D = outs
+    kv = _kv_tensor(kv_len, B, q.device)
+    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
+                                 _ptr(kv), _stream())
+    _check("attn_bwd", st)
+    return dq, dk, dv, D
+
+
+def rowdot(o, do, out=None):
+    """D = rowsum(O o dO) in float32 (the backward's first step alone)."""
+    B, H, N, d = _check_qkv(o, do)
+    D = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if out is None else out
+    st = load_library().attn_bwd_rowdot(_ptr(o), _ptr(do), _ptr(D), B, H, N, d, _DTYPES[o.dtype], _stream())
+    _check("attn_bwd_rowdot", st)
+    return D
+
+
+def bwd_dkdv(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None, kv_len=None, outs=None):
+    """dK, dV alone (the backward's second step), given L and D. Returns ``(dK, dV)``."""
+    B, H, N, d = _check_qkv(q, k, v, do)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dk, dv = (torch.empty_like(k), torch.empty_like(v)) if outs is None else outs
+    kv = _kv_tensor(kv_len, B, q.device)
+    st = load_library().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dk), _ptr(dv),
+                                      B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
+    _check("attn_bwd_dkdv", st)
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None, kv_len=None, out=None):
+    """dQ alone (the backward's third step), given L and D."""
+    B, H, N, d = _check_qkv(q, k, v, do)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if out is None else out
+    kv = _kv_tensor(kv_len, B, q.device)
+    st = load_library().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq), B, H, N, d,
+                                    int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
+    _check("attn_bwd_dq", st)
+    return dq
+
+
+def supported(dtype, d: int) -> bool:
+    return bool(load_library().attn_supported(_DTYPES[dtype], int(d)))

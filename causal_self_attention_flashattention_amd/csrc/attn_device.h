@@ -1,0 +1,183 @@
+// Device-side building blocks shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// Matrix products run on the 32x32 MFMA shapes: v_mfma_f32_32x32x16_bf16 for bf16 operands and
+// v_mfma_f32_32x32x2_f32 for fp32 operands, always accumulating in fp32.  Lane layouts (wave64):
+//   A operand (32 x K):  lane l holds A[l % 32][KPL * (l / 32) + s], s < KPL
+//   B operand (K x 32):  lane l holds B[KPL * (l / 32) + s][l % 32]
+//   accumulator (32x32): lane l, element e holds C[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32]
+// with KPL = 8 (bf16, K = 16) or 1 (fp32, K = 2).
+//
+// An accumulator can be fed back as the B operand of a product that reduces over its rows:
+// each lane already owns one column.  Its rows arrive in a fixed order (see acc_row below), so
+// the operand on the other side, read from LDS, must walk the reduction dimension in that same
+// order; frag_trans does that.  For bf16 it uses ds_read_b64_tr_b16: inside each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte chunks read by lanes 4e + i / 4, e < 4,
+// i.e. a 4 x 16 block of a row-major tile comes back as 16 lanes x 4 rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(3))) char lds_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Masked scores are pushed to this value (log2 domain) before exp2, so their weight underflows
+// to exactly 0 and a row can never produce inf - inf.
+constexpr float kMaskedScore = -1.0e30f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Row (within a 32-row block) held by accumulator element e of lane l.
+__device__ __forceinline__ int acc_row(int e, int half) { return 8 * (e >> 2) + 4 * half + (e & 3); }
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  static constexpr int KPL = 8;     // reduction elements per lane per instruction
+  static constexpr int KSTEP = 16;  // reduction depth of one instruction
+  static constexpr int CALLS32 = 2; // instructions to reduce over a 32-row accumulator block
+  using frag = bf16x8;
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // 32 x KSTEP operand whose rows are tile rows and whose reduction runs along tile columns.
+  // Tile is row-major with a row stride of `ld` elements; `off` is the element offset of
+  // (row0, col0).  One 16-byte LDS read per lane.
+  __device__ __forceinline__ static frag frag_direct(const lds_t* tile, int ld, int off) {
+    const int l = lane_id();
+    const int e = off + (l & 31) * ld + KPL * (l >> 5);
+    return *reinterpret_cast<const __attribute__((address_space(3))) frag*>(tile + 2 * e);
+  }
+  // 32-column operand whose reduction runs down tile rows in accumulator row order, for the
+  // c-th instruction of a 32-row block: slot s of lane l takes tile row
+  // 16c + 8(s/4) + 4(l/32) + s%4 and column l % 32 (relative to `off`).
+  __device__ __forceinline__ static frag frag_trans(const lds_t* tile, int ld, int off, int c) {
+    const int l = lane_id();
+    const int g = l >> 4, j = l & 15;
+    const int row = 16 * c + 4 * (g >> 1) + (j >> 2);
+    const int col = 16 * (g & 1) + 4 * (j & 3);
+    const lds_t* p0 = tile + 2 * (off + row * ld + col);
+    const lds_t* p1 = p0 + 2 * 8 * ld;
+    i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+    i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+    frag f;
+    __builtin_memcpy(reinterpret_cast<char*>(&f), &r0, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &r1, 8);
+    return f;
+  }
+  // Accumulator elements 8c..8c+7, rounded to bf16 (round to nearest even).
+  __device__ __forceinline__ static frag acc_frag(const f32x16& a, int c) {
+    frag f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = (__bf16)a[8 * c + s];
+    return f;
+  }
+  // Operand straight from global memory (row r of a row-major matrix, columns col0..col0+7).
+  __device__ __forceinline__ static frag load_global(const __bf16* rowp, int col0, bool valid) {
+    frag f = {};
+    if (valid) f = *reinterpret_cast<const frag*>(rowp + col0 + KPL * (lane_id() >> 5));
+    return f;
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 2;
+  static constexpr int CALLS32 = 16;
+  using frag = float;
+  __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag frag_direct(const lds_t* tile, int ld, int off) {
+    const int l = lane_id();
+    const int e = off + (l & 31) * ld + (l >> 5);
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(tile + 4 * e);
+  }
+  // Instruction c reduces over accumulator element c: tile row 8(c/4) + 4(l/32) + c%4.
+  __device__ __forceinline__ static frag frag_trans(const lds_t* tile, int ld, int off, int c) {
+    const int l = lane_id();
+    const int row = acc_row(c, l >> 5);
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(tile + 4 * (off + row * ld + (l & 31)));
+  }
+  __device__ __forceinline__ static frag acc_frag(const f32x16& a, int c) { return a[c]; }
+  __device__ __forceinline__ static frag load_global(const float* rowp, int col0, bool valid) {
+    return valid ? rowp[col0 + (lane_id() >> 5)] : 0.0f;
+  }
+};
+
+// Exchange a value with the lane 32 positions away (lanes l and l ^ 32 hold the two halves of
+// an accumulator column).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Cooperative copy of a ROWS x COLS tile (row-major, global row stride = COLS elements) into LDS
+// with row stride LD, 16 bytes per thread per step.  Rows at or beyond `valid_rows` are zero
+// filled.  The copy is split into a register stage (load) and an LDS stage (store) so the global
+// latency can hide behind compute.
+template <typename T, int ROWS, int COLS, int LD, int NTHREADS>
+struct TileCopy {
+  static constexpr int CPR = COLS * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  static constexpr int CHUNKS = ROWS * CPR;
+  static constexpr int PER_THREAD = (CHUNKS + NTHREADS - 1) / NTHREADS;
+  static_assert(COLS * sizeof(T) % 16 == 0, "tile rows must be a multiple of 16 bytes");
+  u32x4 r[PER_THREAD];
+
+  __device__ __forceinline__ void load(const T* g, int valid_rows) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      const int row = c / CPR, cc = c % CPR;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if ((CHUNKS % NTHREADS == 0 || c < CHUNKS) && row < valid_rows)
+        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(g) + (size_t)row * COLS * sizeof(T) + cc * 16);
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(lds_t* tile) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      if (CHUNKS % NTHREADS == 0 || c < CHUNKS) {
+        const int row = c / CPR, cc = c % CPR;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tile + (row * LD) * (int)sizeof(T) + cc * 16) = r[i];
+      }
+    }
+  }
+};
+
+// Zero the columns [COLS, LDZ) of every row of a tile (padding read by 32-wide operand blocks
+// when the head dim is not a multiple of 32).
+template <typename T, int ROWS, int COLS, int LD, int LDZ, int NTHREADS>
+__device__ __forceinline__ void zero_pad_cols(lds_t* tile) {
+  if constexpr (LDZ > COLS) {
+    constexpr int W = LDZ - COLS;
+    for (int i = threadIdx.x; i < ROWS * W; i += NTHREADS) {
+      const int row = i / W, col = COLS + i % W;
+      *reinterpret_cast<__attribute__((address_space(3))) T*>(tile + (row * LD + col) * (int)sizeof(T)) = T(0);
+    }
+  }
+}
+
+// Block index -> logical work item, so that the 8 XCDs (which receive workgroups round-robin)
+// each get a contiguous range of logical items, i.e. whole heads, and share that head's K/V in
+// their own L2.  The grid is padded to a multiple of 8; padding blocks get -1.
+__device__ __forceinline__ int xcd_logical_block(int nlogical) {
+  const int per = (nlogical + 7) >> 3;
+  const int b = blockIdx.x;
+  const int logical = (b & 7) * per + (b >> 3);
+  return logical < nlogical ? logical : -1;
+}
+
+}  // namespace attn

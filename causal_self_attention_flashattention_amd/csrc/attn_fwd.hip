@@ -1,0 +1,217 @@
+// Tiled attention forward with online softmax (gfx950).
+//
+// Computes, per (batch, head), O = softmax(mask(scale * Q K^T)) V and the row logsumexp
+// L_i = log sum_j exp(S_ij) of the scaled, masked scores (natural log), following Algorithm 1
+// ("FlashAttention-2 forward pass") of the CS336 Assignment 2 (systems) handout, §4.1, with
+// the causal mask of its Problem (flash_forward)(c) and an optional per-batch key length.
+//
+// Work decomposition: one workgroup per (head, tile of 32*NW queries); wave w owns 32 queries.
+// Each wave computes the transposed score block S^T = K Q^T (keys on MFMA rows, queries on
+// columns), so each lane holds one query's scores and the row max / row sum are in-lane
+// reductions plus a single exchange with the lane 32 away.  The probabilities are then fed
+// straight from the accumulator as the B operand of O^T += V^T P^T, V^T being read from the
+// row-major V tile with LDS transpose reads.  The exponentials run in the log2 domain with the
+// softmax scale folded into one multiply.
+//
+// Rescaling is lazy: the running max used for exp2 is only moved when a new row max exceeds it
+// by more than kRescaleSlack (log2 units), so most tiles skip the O rescale.  Any stale max is
+// used consistently for the numerator and the denominator, so the result is unchanged (the
+// largest unnormalised weight is bounded by 2^kRescaleSlack, far from overflow).
+#include "attn_device.h"
+#include "launch.h"
+
+namespace attn {
+
+constexpr float kRescaleSlack = 8.0f;
+
+template <typename T, int D, int NW, int BK>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                      const T* __restrict__ V, T* __restrict__ O,
+                                                      float* __restrict__ Lse, int BH, int H, int N,
+                                                      int causal, float scale_log2,
+                                                      const int32_t* __restrict__ kv_len) {
+  using M = Mfma<T>;
+  constexpr int NT = NW * 64;
+  constexpr int QT = 32 * NW;             // queries per workgroup
+  constexpr int DP = (D + 31) / 32 * 32;  // head dim rounded up to a 32-row MFMA block
+  constexpr int NDB = DP / 32;
+  constexpr int KS = D / M::KSTEP;
+  constexpr int NB = BK / 32;
+  constexpr int LD = DP + 16 / (int)sizeof(T);  // LDS row stride (elements), 16 bytes of pad
+  static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * BK * LD * sizeof(T)];
+  lds_t* ktile = (lds_t*)smem;
+  lds_t* vtile = ktile + BK * LD * sizeof(T);
+
+  const int TQ = (N + QT - 1) / QT;
+  const int logical = xcd_logical_block(BH * TQ);
+  if (logical < 0) return;
+  const int bh = logical / TQ;
+  const int qt = TQ - 1 - logical % TQ;  // heaviest (causal) tiles of a head first
+  const int b = bh / H;
+  int kv = N;
+  if (kv_len) kv = min(max(kv_len[b], 1), N);
+
+  const size_t base = (size_t)bh * N * D;
+  Q += base; K += base; V += base; O += base;
+  Lse += (size_t)bh * N;
+
+  const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
+  const int q0 = qt * QT;
+  const int qw = q0 + 32 * w;  // first query of this wave
+  const int q = qw + col;      // this lane's query
+  const int qw_last = min(qw + 31, N - 1);
+
+  int kend = kv;
+  if (causal) kend = min(kend, q0 + QT);
+  const int nkt = (kend + BK - 1) / BK;
+
+  typename M::frag qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = M::load_global(Q + (size_t)min(q, N - 1) * D, ks * M::KSTEP, q < N);
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  TileCopy<T, BK, D, LD, NT> kc, vc;
+  zero_pad_cols<T, BK, D, LD, DP, NT>(vtile);
+  kc.load(K, kend);
+  vc.load(V, kend);
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    kc.store(ktile);
+    vc.store(vtile);
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      kc.load(K + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
+      vc.load(V + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
+    }
+    const int k0 = kt * BK;
+    if (qw >= N || (causal && k0 > qw_last)) continue;  // no live query, or tile above the diagonal
+
+    f32x16 s[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      s[nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[nb] = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+    }
+
+    const bool need_mask = (causal && k0 + BK - 1 > qw) || (k0 + BK > kv);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[nb][e] * scale_log2;
+        if (need_mask) {
+          const int key = k0 + nb * 32 + acc_row(e, half);
+          if ((causal && key > q) || key >= kv) x = kMaskedScore;
+        }
+        s[nb][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, swap_halves(mx));
+    if (mx > m_run + kRescaleSlack) {
+      const float alpha = fast_exp2(m_run - mx);
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      l_part *= alpha;
+      m_run = mx;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(s[nb][e] - m_run);
+        s[nb][e] = p;
+        l_part += p;
+      }
+
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < M::CALLS32; ++c) {
+        const typename M::frag pf = M::acc_frag(s[nb], c);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
+      }
+  }
+
+  const float l_tot = l_part + swap_halves(l_part);
+  const float inv = 1.0f / l_tot;
+  if (q < N) {
+    T* orow = O + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int d0 = db * 32 + 8 * m + 4 * half;
+        if (D % 32 == 0 || d0 < D) {
+          T v4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v4[r] = (T)(o[db][4 * m + r] * inv);
+          if constexpr (sizeof(T) == 2) {
+            uint2 u;
+            __builtin_memcpy(&u, v4, 8);
+            *reinterpret_cast<uint2*>(orow + d0) = u;
+          } else {
+            uint4 u;
+            __builtin_memcpy(&u, v4, 16);
+            *reinterpret_cast<uint4*>(orow + d0) = u;
+          }
+        }
+      }
+    if (half == 0) Lse[q] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+template <typename T, int D, int NW, int BK>
+static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O,
+                               float* L, hipStream_t stream) {
+  constexpr int QT = 32 * NW;
+  const int TQ = (p.N + QT - 1) / QT;
+  const int nlog = p.B * p.H * TQ;
+  const int grid = (nlog + 7) / 8 * 8;
+  const float sl2 = p.scale * kLog2e;
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
+                     (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len);
+  return hipGetLastError();
+}
+
+bool fwd_supported(int dtype, int d) {
+  (void)dtype;
+  return d == 16 || d == 32 || d == 64 || d == 80 || d == 128;
+}
+
+hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K, const void* V, void* O,
+                      float* L, hipStream_t s) {
+  if (dtype == kBF16) {
+    switch (p.d) {
+      case 16: return launch_fwd_t<__bf16, 16, 4, 64>(p, Q, K, V, O, L, s);
+      case 32: return launch_fwd_t<__bf16, 32, 4, 64>(p, Q, K, V, O, L, s);
+      case 64: return launch_fwd_t<__bf16, 64, 4, 64>(p, Q, K, V, O, L, s);
+      case 80: return launch_fwd_t<__bf16, 80, 4, 64>(p, Q, K, V, O, L, s);
+      case 128: return launch_fwd_t<__bf16, 128, 4, 64>(p, Q, K, V, O, L, s);
+    }
+  } else if (dtype == kF32) {
+    switch (p.d) {
+      case 16: return launch_fwd_t<float, 16, 4, 32>(p, Q, K, V, O, L, s);
+      case 32: return launch_fwd_t<float, 32, 4, 32>(p, Q, K, V, O, L, s);
+      case 64: return launch_fwd_t<float, 64, 4, 32>(p, Q, K, V, O, L, s);
+      case 80: return launch_fwd_t<float, 80, 4, 32>(p, Q, K, V, O, L, s);
+      case 128: return launch_fwd_t<float, 128, 4, 32>(p, Q, K, V, O, L, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,36 @@
+// Host-side launchers for the attention kernels (internal to libattn; the public C ABI is
+// include/attn.h).  Each launcher only enqueues work on `stream`; it returns hipSuccess, or
+// hipErrorInvalidValue when no kernel exists for the (dtype, head dim) pair, or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+struct Problem {
+  int B, H, N, d;
+  int causal;
+  float scale;
+  const int32_t* kv_len;  // device int32[B] or nullptr
+};
+
+bool fwd_supported(int dtype, int d);
+bool bwd_supported(int dtype, int d);
+
+hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
+                      void* O, float* L, hipStream_t stream);
+
+hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void* dO, float* Dv,
+                         hipStream_t stream);
+
+hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
+                       const void* dO, const float* L, const float* Dv, void* dK, void* dV,
+                       hipStream_t stream);
+
+hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
+                     const void* dO, const float* L, const float* Dv, void* dQ, hipStream_t stream);
+
+}  // namespace attn

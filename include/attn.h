@@ -1,0 +1,107 @@
+/* attn.h -- C ABI of libattn: tiled causal / key-padded self-attention, forward and backward,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (notation of the CS336 Assignment 2 (systems) handout, §4.1 "Optimizing
+ * Attention with FlashAttention-2"):
+ *   forward  (eq. 1, eqs. 4-6, eq. 12, Algorithm 1):
+ *     S = scale * Q K^T, masked entries removed, P = row softmax(S), O = P V,
+ *     L_i = log sum_j exp(S_ij) over the unmasked entries of row i (natural log).
+ *   backward (eqs. 13-19, "backward pass with recomputation"):
+ *     D_i = sum_c O_ic dO_ic, P_ij = exp(S_ij - L_i), dV = P^T dO, dP = dO V^T,
+ *     dS_ij = P_ij (dP_ij - D_i), dQ = scale dS K, dK = scale dS^T Q.
+ *   masks: causal (Problem (flash_forward)(c)): key j is masked for query i when j > i, with
+ *     equal query and key lengths N; key padding: keys j >= kv_len[b] are masked for every
+ *     query of batch row b.  Queries are never masked.
+ *
+ * Layout: Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] (d fastest) in the
+ * element type `dtype`; L and D are dense [B, H, N] float32.  `kv_len` is a device int32[B] or
+ * NULL (no padding).  All pointers are device pointers, 16-byte aligned, owned by the caller;
+ * the library allocates nothing and keeps no per-call state.
+ *
+ * Execution: every call only enqueues kernels on `stream` (NULL = the default stream) and
+ * returns without synchronising the host; faults inside a kernel surface at the caller's next
+ * synchronisation.  Results are bitwise reproducible (no atomics).
+ *
+ * Errors: each call validates its arguments before launching anything and returns an
+ * attn_status; on any negative status nothing has been enqueued (except ATTN_E_LAUNCH, which
+ * reports the HIP launch error of a kernel).  No exception crosses the ABI.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,    /* a required pointer is NULL */
+  ATTN_E_SHAPE = -2,   /* B, H, N or d < 1, or B*H*N*d >= 2^31 elements */
+  ATTN_E_HEADDIM = -3, /* no kernel for this head dim (supported: 16, 32, 64, 80, 128) */
+  ATTN_E_DTYPE = -4,   /* dtype is not an attn_dtype */
+  ATTN_E_ALIGN = -5,   /* a pointer is not 16-byte aligned */
+  ATTN_E_ALIAS = -6,   /* an output buffer overlaps an input or another output */
+  ATTN_E_LAUNCH = -7,  /* a kernel launch failed (HIP error) */
+  ATTN_E_SCALE = -8    /* scale is not a finite number */
+} attn_status;
+
+/* Forward pass (Algorithm 1 of the handout, §4.1, with the causal flag of Problem
+ * (flash_forward)(c)).
+ *   Q, K, V  in : [B,H,N,d] dtype
+ *   O        out: [B,H,N,d] dtype, softmax(mask(scale Q K^T)) V
+ *   L        out: [B,H,N] float32, natural-log logsumexp of the scaled, masked scores
+ *   causal      : 0 or non-zero
+ *   scale       : softmax scale, normally 1/sqrt(d)
+ *   kv_len      : device int32[B], 1 <= kv_len[b] <= N (values outside are clamped), or NULL
+ * O and L must not overlap any input or each other. */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,
+             int causal, float scale, int dtype, const int32_t* kv_len, hipStream_t stream);
+
+/* Backward pass (eqs. 13-19 of the handout, §4.1; the two-kernel split of §4.2.3 that
+ * recomputes P once for dK/dV and once for dQ).
+ *   Q, K, V, O, dO in : [B,H,N,d] dtype (O and L as returned by attn_fwd for the same inputs)
+ *   L              in : [B,H,N] float32
+ *   dQ, dK, dV     out: [B,H,N,d] dtype
+ *   D              out: [B,H,N] float32 workspace, receives rowsum(O o dO)
+ * Other arguments as for attn_fwd.  Outputs must not overlap inputs or each other. */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+             void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+             int dtype, const int32_t* kv_len, hipStream_t stream);
+
+/* The backward's first step alone: D_i = sum_c O_ic dO_ic in float32 (handout §4.1, the D
+ * vector of the backward pass with recomputation).  O, dO: [B,H,N,d] dtype; D: [B,H,N] float32. */
+int attn_bwd_rowdot(const void* O, const void* dO, float* D, int B, int H, int N, int d, int dtype,
+                    hipStream_t stream);
+
+/* The backward's second step alone: dK and dV for every key tile (eqs. 13-17 and 19 of the
+ * handout, §4.1), P recomputed from L, D taken from attn_bwd_rowdot.  Arguments as for attn_bwd;
+ * D is an input here.  attn_bwd = attn_bwd_rowdot, then attn_bwd_dkdv, then attn_bwd_dq. */
+int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
+                  void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, int dtype,
+                  const int32_t* kv_len, hipStream_t stream);
+
+/* The backward's third step alone: dQ for every query tile (eqs. 13-14, 16-18 of the handout,
+ * §4.1), P recomputed a second time so that no two workgroups write the same output. */
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
+                void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype, const int32_t* kv_len,
+                hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* 1 if a kernel exists for (dtype, d), else 0. */
+int attn_supported(int dtype, int d);
+
+/* ABI version: 10000 * major + 100 * minor + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

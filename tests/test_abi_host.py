@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every entry point
+include/attn.h declares, and rejects bad arguments with the documented status before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_self_attention_flashattention_amd.binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+ATTN_OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH, E_SCALE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bnd.LIB_PATH):
+        pytest.fail("libattn.so is not built (run __graft_entry__.build())")
+    return bnd.load_library()
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(bnd.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libattn.so does not export {name}"
+
+
+def test_exported_symbols_have_c_linkage():
+    out = os.popen(f"nm -D --defined-only {bnd.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} missing or mangled in the dynamic symbol table"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_version() == 10000
+    for st in (ATTN_OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH, E_SCALE):
+        s = bnd.status_string(st)
+        assert s and s != "unknown status"
+    assert bnd.status_string(12345) == "unknown status"
+
+
+def test_supported_head_dims(lib):
+    for dt in (0, 1):
+        for d in (16, 32, 64, 80, 128):
+            assert lib.attn_supported(dt, d) == 1
+        for d in (0, 8, 48, 96, 256):
+            assert lib.attn_supported(dt, d) == 0
+    assert lib.attn_supported(2, 64) == 0
+
+
+# Fake, never-dereferenced device addresses: validation must reject these calls before launching.
+A = 1 << 20
+SZ = 1 << 28
+
+
+def _fwd(lib, Q=A, K=A + SZ, V=A + 2 * SZ, O=A + 3 * SZ, L=A + 4 * SZ, B=1, H=1, N=16, d=64, causal=1,
+         scale=0.125, dtype=1, kv=None):
+    return lib.attn_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, kv, None)
+
+
+def _bwd(lib, **kw):
+    p = dict(Q=A, K=A + SZ, V=A + 2 * SZ, O=A + 3 * SZ, dO=A + 4 * SZ, L=A + 5 * SZ, dQ=A + 6 * SZ,
+             dK=A + 7 * SZ, dV=A + 8 * SZ, D=A + 9 * SZ, B=1, H=1, N=16, d=64, causal=1, scale=0.125, dtype=1, kv=None)
+    p.update(kw)
+    return lib.attn_bwd(p["Q"], p["K"], p["V"], p["O"], p["dO"], p["L"], p["dQ"], p["dK"], p["dV"], p["D"], p["B"],
+                        p["H"], p["N"], p["d"], p["causal"], p["scale"], p["dtype"], p["kv"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), E_NULL), (dict(O=None), E_NULL), (dict(L=None), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(d=0), E_SHAPE),
+    (dict(B=1024, H=1024, N=1024, d=64), E_SHAPE),
+    (dict(d=96), E_HEADDIM), (dict(d=48), E_HEADDIM), (dict(dtype=7), E_DTYPE),
+    (dict(scale=float("nan")), E_SCALE), (dict(scale=float("inf")), E_SCALE),
+    (dict(Q=A + 8), E_ALIGN), (dict(L=A + 4 * SZ + 4), E_ALIGN),
+    (dict(O=A + 2 * SZ + 16), E_ALIAS),   # O overlaps V
+    (dict(L=A + 3 * SZ + 64), E_ALIAS),   # L inside O
+    (dict(kv=A + 3 * SZ), E_ALIAS),       # kv_len inside O
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), E_NULL), (dict(D=None), E_NULL), (dict(dV=None), E_NULL),
+    (dict(N=0), E_SHAPE), (dict(d=100), E_HEADDIM), (dict(dtype=-1), E_DTYPE),
+    (dict(dK=A + 7 * SZ + 2), E_ALIGN),
+    (dict(dQ=A), E_ALIAS),                # dQ == Q
+    (dict(dK=A + 6 * SZ), E_ALIAS),       # dK == dQ
+    (dict(D=A + 5 * SZ), E_ALIAS),        # D == L
+    (dict(scale=float("-inf")), E_SCALE),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_rowdot_rejects_bad_arguments(lib):
+    assert lib.attn_bwd_rowdot(None, A + SZ, A + 2 * SZ, 1, 1, 16, 64, 1, None) == E_NULL
+    assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 16, 24, 1, None) == E_HEADDIM
+    assert lib.attn_bwd_rowdot(A, A + SZ, A + 16, 1, 1, 16, 64, 1, None) == E_ALIAS
+    assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 16, 64, 3, None) == E_DTYPE
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        bnd.fwd(q, q, q)

@@ -1,0 +1,171 @@
+"""GPU checks against closed forms and invariants fixed by the definitions (no oracle needed),
+plus determinism, guard bands and the equivalence of attn_bwd with its three sub-steps."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_flashattention_amd as attn
+from causal_self_attention_flashattention_amd.inputs import make_inputs
+
+from attn_testutil import announce, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal,kv", [(True, None), (True, 150), (False, 97)])
+def test_zero_query_gives_prefix_mean(dtype, d, causal, kv):
+    """Q = 0: S = 0, so O_i is the mean of the visible V rows and L_i = ln(#visible keys)."""
+    require_gpu()
+    B, H, N = 1, 2, 300
+    announce(f"zero-query dtype={dtype} d={d} causal={causal} kv={kv}")
+    inp = to_dev(make_inputs(B, H, N, d, dtype, seed=21, kv_len=kv))
+    q = torch.zeros_like(inp["q"])
+    o, L = attn.fwd(q, inp["k"], inp["v"], causal=causal, kv_len=inp["kv_len"])
+    v = inp["v"].double().cpu().numpy()
+    o, L = o.double().cpu().numpy(), L.double().cpu().numpy()
+    hi = np.full(N, N if kv is None else kv)
+    if causal:
+        hi = np.minimum(hi, np.arange(1, N + 1))
+    csum = np.cumsum(v, axis=2)
+    ref = csum[:, :, hi - 1, :] / hi[None, None, :, None]
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert np.abs(o - ref).max() <= tol + (1e-2 if dtype == "bf16" else 0) * np.abs(ref).max()
+    assert np.abs(L - np.log(hi)[None, None, :]).max() <= (1e-5 if dtype == "f32" else 1e-3)
+
+
+def test_identity_values_expose_probabilities():
+    """V = I (N = d = 64, float32): O = P, so each row sums to 1 and masked weights are exactly 0."""
+    require_gpu()
+    N = d = 64
+    announce("identity-V N=d=64 f32")
+    inp = to_dev(make_inputs(1, 1, N, d, "f32", seed=22))
+    v = torch.eye(N, device="cuda").reshape(1, 1, N, d).contiguous()
+    for causal, kv in ((True, None), (False, 40), (True, 50)):
+        o, _ = attn.fwd(inp["q"], inp["k"], v, causal=causal, kv_len=None if kv is None else [kv])
+        p = o[0, 0].double().cpu().numpy()
+        assert np.abs(p.sum(1) - 1).max() < 1e-5
+        i, j = np.arange(N)[:, None], np.arange(N)[None, :]
+        masked = np.zeros((N, N), dtype=bool)
+        if causal:
+            masked |= j > i
+        if kv is not None:
+            masked |= j >= kv
+        assert np.all(p[masked] == 0.0)
+        assert np.all(p[~masked] > 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_padded_keys_have_no_effect(dtype):
+    """Randomising K_j, V_j for j >= kv leaves O, L, dQ bitwise unchanged; dK_j = dV_j = 0 exactly."""
+    require_gpu()
+    B, H, N, d, kv = 2, 2, 333, 64, [250, 333]
+    announce(f"padding-invariance dtype={dtype}")
+    a = to_dev(make_inputs(B, H, N, d, dtype, seed=23, kv_len=kv))
+    b = dict(a)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    k2, v2 = a["k"].clone(), a["v"].clone()
+    k2[0, :, 250:] = torch.randn(k2[0, :, 250:].shape, generator=gen, device="cuda").to(k2.dtype) * 3
+    v2[0, :, 250:] = torch.randn(v2[0, :, 250:].shape, generator=gen, device="cuda").to(v2.dtype) * 3
+    b["k"], b["v"] = k2, v2
+    outs = []
+    for x in (a, b):
+        o, L = attn.fwd(x["q"], x["k"], x["v"], causal=True, kv_len=x["kv_len"])
+        dq, dk, dv, D = attn.bwd(x["q"], x["k"], x["v"], o, x["do"], L, causal=True, kv_len=x["kv_len"])
+        outs.append((o, L, dq, dk, dv))
+    torch.cuda.synchronize()
+    for t1, t2 in zip(outs[0][:3], outs[1][:3]):
+        assert torch.equal(t1, t2)
+    for t in outs[1][3:]:
+        assert (t[0, :, 250:] == 0).all()
+
+
+def test_causality_is_bitwise():
+    """Changing K_j, V_j for j > cut leaves rows <= cut of O and L bitwise unchanged."""
+    require_gpu()
+    B, H, N, d, cut = 1, 2, 400, 128, 211
+    announce("causality bf16 d=128")
+    a = to_dev(make_inputs(B, H, N, d, "bf16", seed=24))
+    k2, v2 = a["k"].clone(), a["v"].clone()
+    k2[:, :, cut + 1:] = -k2[:, :, cut + 1:] * 2
+    v2[:, :, cut + 1:] = v2[:, :, cut + 1:] + 1
+    o1, l1 = attn.fwd(a["q"], a["k"], a["v"], causal=True)
+    o2, l2 = attn.fwd(a["q"], k2, v2, causal=True)
+    assert torch.equal(o1[:, :, : cut + 1], o2[:, :, : cut + 1])
+    assert torch.equal(l1[:, :, : cut + 1], l2[:, :, : cut + 1])
+    assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 80), ("f32", 128)])
+def test_deterministic_and_substeps_equal_bwd(dtype, d):
+    """Two runs are bitwise equal (no atomics), and attn_bwd == rowdot, then dK/dV, then dQ."""
+    require_gpu()
+    B, H, N = 2, 3, 517
+    announce(f"determinism dtype={dtype} d={d}")
+    x = to_dev(make_inputs(B, H, N, d, dtype, seed=25, kv_len=[517, 400]))
+    runs = []
+    for _ in range(2):
+        o, L = attn.fwd(x["q"], x["k"], x["v"], causal=True, kv_len=x["kv_len"])
+        runs.append((o, L) + attn.bwd(x["q"], x["k"], x["v"], o, x["do"], L, causal=True, kv_len=x["kv_len"]))
+    for t1, t2 in zip(*runs):
+        assert torch.equal(t1, t2)
+    o, L = runs[0][:2]
+    D = attn.rowdot(o, x["do"])
+    dk, dv = attn.bwd_dkdv(x["q"], x["k"], x["v"], x["do"], L, D, causal=True, kv_len=x["kv_len"])
+    dq = attn.bwd_dq(x["q"], x["k"], x["v"], x["do"], L, D, causal=True, kv_len=x["kv_len"])
+    torch.cuda.synchronize()
+    for got, want in zip((dq, dk, dv, D), runs[0][2:]):
+        assert torch.equal(got, want)
+
+
+def _guarded(shape, dtype, pad_elems=4096):
+    """A contiguous tensor of `shape` inside a larger buffer whose margins hold a canary."""
+    n = math.prod(shape)
+    buf = torch.empty(pad_elems * 2 + n, dtype=dtype, device="cuda")
+    buf.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).fill_(0x7F5A if dtype == torch.bfloat16
+                                                                              else 0x7F5A5A5A)
+    return buf, buf[pad_elems: pad_elems + n].view(shape)
+
+
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 80, 211), ("bf16", 128, 64), ("f32", 64, 130)])
+def test_outputs_stay_inside_their_buffers(dtype, d, N):
+    """Guard bands around O, L, dQ, dK, dV, D keep their canary after fwd + bwd."""
+    require_gpu()
+    B, H = 2, 2
+    announce(f"guard-bands dtype={dtype} d={d} N={N}")
+    x = to_dev(make_inputs(B, H, N, d, dtype, seed=26, kv_len=[N, N - 7]))
+    t = DT[dtype]
+    bufs = {}
+    for name, shape, dt in (("o", (B, H, N, d), t), ("L", (B, H, N), torch.float32), ("dq", (B, H, N, d), t),
+                            ("dk", (B, H, N, d), t), ("dv", (B, H, N, d), t), ("D", (B, H, N), torch.float32)):
+        bufs[name] = _guarded(shape, dt)
+    snap = {k: v[0].clone() for k, v in bufs.items()}
+    o, L = attn.fwd(x["q"], x["k"], x["v"], causal=True, kv_len=x["kv_len"], out=bufs["o"][1], lse=bufs["L"][1])
+    attn.bwd(x["q"], x["k"], x["v"], o, x["do"], L, causal=True, kv_len=x["kv_len"],
+             outs=(bufs["dq"][1], bufs["dk"][1], bufs["dv"][1], bufs["D"][1]))
+    torch.cuda.synchronize()
+    for name, (buf, view) in bufs.items():
+        pad = 4096
+        n = view.numel()
+        assert torch.equal(buf[:pad], snap[name][:pad]), f"{name}: wrote before its buffer"
+        assert torch.equal(buf[pad + n:], snap[name][pad + n:]), f"{name}: wrote past its buffer"
+        assert torch.isfinite(view).all()
+
+
+def test_abi_errors_on_device_tensors():
+    """Validation errors surface as AttnError with the documented status; nothing is launched."""
+    require_gpu()
+    x = to_dev(make_inputs(1, 1, 64, 64, "bf16", seed=27))
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(x["q"], x["k"], x["v"], out=x["q"])  # O aliases Q
+    assert e.value.status == -6
+    q96 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(q96, q96.clone(), q96.clone())
+    assert e.value.status == -3
