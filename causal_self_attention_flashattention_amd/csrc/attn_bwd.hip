@@ -51,10 +51,11 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (head, 32*NW keys); loop over query tiles of BQ rows.
+// dK, dV: one workgroup per (head, 32*NW keys); loop over query tiles of BQ rows, double
+// buffered in LDS together with the tile's L*log2(e) and D values.
 
-template <typename T, int D, int NW, int BQ>
-__global__ __launch_bounds__(NW * 64) void dkdv_kernel(
+template <typename T, int D, int NW, int BQ, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
     int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
@@ -66,12 +67,12 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   constexpr int KS = D / M::KSTEP;
   constexpr int NQB = BQ / 32;
   constexpr int LD = DP + 16 / (int)sizeof(T);
+  constexpr int TILE = BQ * LD * (int)sizeof(T);
+  constexpr int STAGE = 2 * TILE + 2 * BQ * (int)sizeof(float);  // Q tile, dO tile, L row, D row
+  static_assert(2 * BQ <= NT, "one thread per staged L / D value");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BQ * LD * sizeof(T) + 2 * BQ * sizeof(float)];
-  lds_t* qtile = (lds_t*)smem;
-  lds_t* otile = qtile + BQ * LD * sizeof(T);  // dO tile
-  float* lrow = reinterpret_cast<float*>(smem + 2 * BQ * LD * sizeof(T));  // L * log2(e), per query
-  float* drow = lrow + BQ;                                                 // D, per query
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  lds_t* lds = (lds_t*)smem;
 
   const int TK = (N + KT - 1) / KT;
   const int logical = xcd_logical_block(BH * TK);
@@ -83,92 +84,117 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   if (kv_len) kv = min(max(kv_len[b], 1), N);
 
   const size_t base = (size_t)bh * N * D;
-  Q += base; K += base; V += base; dO += base; dK += base; dV += base;
-  Lse += (size_t)bh * N;
-  Dv += (size_t)bh * N;
+  dK += base; dV += base;
 
   const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
   const int k0 = kt * KT;
   const int kw = k0 + 32 * w;  // first key of this wave
   const int key = kw + col;    // this lane's key
   const bool wave_live = kw < kv;
+  // This lane's key is visible to queries q with qmin <= q < N (and never if key >= kv).
+  const int qmin = key >= kv ? N : (causal ? key : 0);
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
   if (k0 < kv) {
+    const uint32_t tbytes = (uint32_t)(N * D * sizeof(T));
+    const auto rk = make_rsrc(K + base, tbytes);
+    const auto rv = make_rsrc(V + base, tbytes);
+    const auto rq = make_rsrc(Q + base, tbytes);
+    const auto ro = make_rsrc(dO + base, tbytes);
+    const auto rl = make_rsrc(Lse + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
+    const auto rd = make_rsrc(Dv + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
     typename M::frag kf[KS], vf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = M::load_global(K + (size_t)min(key, N - 1) * D, ks * M::KSTEP, key < N);
-      vf[ks] = M::load_global(V + (size_t)min(key, N - 1) * D, ks * M::KSTEP, key < N);
+      kf[ks] = frag_global<T>(rk, key, D, ks * M::KSTEP);
+      vf[ks] = frag_global<T>(rv, key, D, ks * M::KSTEP);
     }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
+    const int nqt = TQ - qt0;
 
+    if constexpr (DP > D) {
+      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds);
+      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + TILE);
+      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + STAGE);
+      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + STAGE + TILE);
+    }
     TileCopy<T, BQ, D, LD, NT> qc, oc;
-    zero_pad_cols<T, BQ, D, LD, DP, NT>(qtile);
-    zero_pad_cols<T, BQ, D, LD, DP, NT>(otile);
-    qc.load(Q + (size_t)qt0 * BQ * D, N - qt0 * BQ);
-    oc.load(dO + (size_t)qt0 * BQ * D, N - qt0 * BQ);
-    for (int qt = qt0; qt < TQ; ++qt) {
-      const int q0 = qt * BQ;
-      __syncthreads();
-      qc.store(qtile);
-      oc.store(otile);
-      for (int i = threadIdx.x; i < BQ; i += NT) {
-        const int qq = q0 + i;
-        lrow[i] = qq < N ? Lse[qq] * kLog2e : 0.f;
-        drow[i] = qq < N ? Dv[qq] : 0.f;
-      }
-      __syncthreads();
-      if (qt + 1 < TQ) {
-        qc.load(Q + (size_t)(qt + 1) * BQ * D, N - (qt + 1) * BQ);
-        oc.load(dO + (size_t)(qt + 1) * BQ * D, N - (qt + 1) * BQ);
-      }
-      if (!wave_live) continue;
+    float lrd = 0.f;  // one staged L*log2(e) (threads < BQ) or D (threads BQ..2BQ-1) value
+    auto load_stage = [&](int qt) {
+      qc.load(rq, qt * BQ);
+      oc.load(ro, qt * BQ);
+      const int t = threadIdx.x;
+      if (t < BQ) lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (qt * BQ + t) * 4, 0, 0)) * kLog2e;
+      else if (t < 2 * BQ) lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (qt * BQ + t - BQ) * 4, 0, 0));
+    };
+    auto store_stage = [&](lds_t* st) {
+      qc.store(st);
+      oc.store(st + TILE);
+      if (threadIdx.x < 2 * BQ)
+        reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] = lrd;
+    };
+    load_stage(qt0);
+    store_stage(lds);
+    __syncthreads();
+    if (nqt > 1) load_stage(qt0 + 1);
+
+    for (int it = 0; it < nqt; ++it) {
+      const int q0 = (qt0 + it) * BQ;
+      const lds_t* qtile = lds + (it & 1) * STAGE;
+      const lds_t* otile = qtile + TILE;
+      const __attribute__((address_space(3))) float* lrow =
+          reinterpret_cast<const __attribute__((address_space(3))) float*>(qtile + 2 * TILE);
+      const __attribute__((address_space(3))) float* drow = lrow + BQ;
+      if (wave_live) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qb0 = q0 + qb * 32;
-        if (qb0 >= N || (causal && qb0 + 31 < kw)) continue;  // past the end, or all queries before this wave's keys
-        f32x16 s = f32x16{}, dp = f32x16{};
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int qb0 = q0 + qb * 32;
+          if (qb0 >= N || (causal && qb0 + 31 < kw)) continue;  // past the end, or before this wave's keys
+          f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = M::mma(M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP), kf[ks], s);
-          dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
-        }
-        const bool need_mask = (causal && kw + 31 > qb0) || (kw + 32 > kv) || (qb0 + 32 > N);
+          for (int ks = 0; ks < KS; ++ks) {
+            s = M::mma(M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP), kf[ks], s);
+            dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
+          }
+          const bool need_mask = (causal && kw + 31 > qb0) || (kw + 32 > kv) || (qb0 + 32 > N);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r0 = qb * 32 + 8 * m + 4 * half;
-          const float4 lv = *reinterpret_cast<const float4*>(lrow + r0);
-          const float4 dd = *reinterpret_cast<const float4*>(drow + r0);
-          const float la[4] = {lv.x, lv.y, lv.z, lv.w};
-          const float da[4] = {dd.x, dd.y, dd.z, dd.w};
+          for (int m = 0; m < 4; ++m) {
+            const int r0 = qb * 32 + 8 * m + 4 * half;
+            const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lrow + r0);
+            const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + r0);
+            const float la[4] = {lv.x, lv.y, lv.z, lv.w};
+            const float da[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * m + r;
-            float p = fast_exp2(s[e] * scale_log2 - la[r]);
-            if (need_mask) {
-              const int qq = q0 + r0 + r;
-              if ((causal && key > qq) || key >= kv || qq >= N) p = 0.f;
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * m + r;
+              float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -la[r]));
+              if (need_mask) {
+                const int qq = q0 + r0 + r;
+                p = (qq < qmin || qq >= N) ? 0.f : p;
+              }
+              s[e] = p;
+              dp[e] = p * (dp[e] - da[r]);
             }
-            s[e] = p;
-            dp[e] = p * (dp[e] - da[r]);
           }
-        }
 #pragma unroll
-        for (int c = 0; c < M::CALLS32; ++c) {
-          const typename M::frag pf = M::acc_frag(s, c);
-          const typename M::frag sf = M::acc_frag(dp, c);
+          for (int c = 0; c < M::CALLS32; ++c) {
+            const typename M::frag pf = M::acc_frag(s, c);
+            const typename M::frag sf = M::acc_frag(dp, c);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dv[db] = M::mma(M::frag_trans(otile, LD, qb * 32 * LD + db * 32, c), pf, dv[db]);
-            dk[db] = M::mma(M::frag_trans(qtile, LD, qb * 32 * LD + db * 32, c), sf, dk[db]);
+            for (int db = 0; db < NDB; ++db) {
+              dv[db] = M::mma(M::frag_trans(otile, LD, qb * 32 * LD + db * 32, c), pf, dv[db]);
+              dk[db] = M::mma(M::frag_trans(qtile, LD, qb * 32 * LD + db * 32, c), sf, dk[db]);
+            }
           }
         }
       }
+      if (it + 1 < nqt) store_stage(lds + ((it + 1) & 1) * STAGE);
+      __syncthreads();
+      if (it + 2 < nqt) load_stage(qt0 + it + 2);
     }
   }
 
@@ -206,10 +232,10 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// dQ: one workgroup per (head, 32*NW queries); loop over key tiles of BK rows.
+// dQ: one workgroup per (head, 32*NW queries); loop over key tiles of BK rows, double buffered.
 
-template <typename T, int D, int NW, int BK>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(
+template <typename T, int D, int NW, int BK, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dQ, int BH, int H, int N,
     int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
@@ -221,10 +247,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;
   constexpr int LD = DP + 16 / (int)sizeof(T);
+  constexpr int TILE = BK * LD * (int)sizeof(T);
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BK * LD * sizeof(T)];
-  lds_t* ktile = (lds_t*)smem;
-  lds_t* vtile = ktile + BK * LD * sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  lds_t* lds = (lds_t*)smem;
 
   const int TQ = (N + QT - 1) / QT;
   const int logical = xcd_logical_block(BH * TQ);
@@ -236,74 +262,92 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   if (kv_len) kv = min(max(kv_len[b], 1), N);
 
   const size_t base = (size_t)bh * N * D;
-  Q += base; K += base; V += base; dO += base; dQ += base;
-  Lse += (size_t)bh * N;
-  Dv += (size_t)bh * N;
+  dQ += base;
 
   const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
   const int q0 = qt * QT;
   const int qw = q0 + 32 * w;
   const int q = qw + col;
   const int qw_last = min(qw + 31, N - 1);
+  const bool wave_live = qw < N;
+  const int lim = causal ? min(q, kv - 1) : kv - 1;
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
   const int nkt = (kend + BK - 1) / BK;
 
+  const uint32_t tbytes = (uint32_t)(N * D * sizeof(T));
+  const auto rq = make_rsrc(Q + base, tbytes);
+  const auto ro = make_rsrc(dO + base, tbytes);
+  const auto rk = make_rsrc(K + base, (uint32_t)(kend * D * sizeof(T)));
+  const auto rv = make_rsrc(V + base, (uint32_t)(kend * D * sizeof(T)));
+
   typename M::frag qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = M::load_global(Q + (size_t)min(q, N - 1) * D, ks * M::KSTEP, q < N);
-    of[ks] = M::load_global(dO + (size_t)min(q, N - 1) * D, ks * M::KSTEP, q < N);
+    qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
+    of[ks] = frag_global<T>(ro, q, D, ks * M::KSTEP);
   }
-  const float lq = q < N ? Lse[q] * kLog2e : 0.f;
-  const float dq_ = q < N ? Dv[q] : 0.f;
+  const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : 0.f;
+  const float dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
+  if constexpr (DP > D) {
+    zero_pad_cols<T, BK, D, LD, DP, NT>(lds);
+    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 2 * TILE);
+  }
   TileCopy<T, BK, D, LD, NT> kc, vc;
-  zero_pad_cols<T, BK, D, LD, DP, NT>(ktile);
-  kc.load(K, kend);
-  vc.load(V, kend);
+  kc.load(rk, 0);
+  vc.load(rv, 0);
+  kc.store(lds);
+  vc.store(lds + TILE);
+  __syncthreads();
+  if (nkt > 1) {
+    kc.load(rk, BK);
+    vc.load(rv, BK);
+  }
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    kc.store(ktile);
-    vc.store(vtile);
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      kc.load(K + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
-      vc.load(V + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
-    }
-    if (qw >= N) continue;
+    const lds_t* ktile = lds + (kt & 1) * 2 * TILE;
+    const lds_t* vtile = ktile + TILE;
+    if (wave_live) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int kb0 = kt * BK + nb * 32;
-      if (kb0 >= kend || (causal && kb0 > qw_last)) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int nb = 0; nb < NB; ++nb) {
+        const int kb0 = kt * BK + nb * 32;
+        if (kb0 >= kend || (causal && kb0 > qw_last)) continue;
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s);
-        dp = M::mma(M::frag_direct(vtile, LD, nb * 32 * LD + ks * M::KSTEP), of[ks], dp);
-      }
-      const bool need_mask = (causal && kb0 + 31 > qw) || (kb0 + 32 > kv);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = fast_exp2(s[e] * scale_log2 - lq);
-        if (need_mask) {
-          const int kk = kb0 + acc_row(e, half);
-          if ((causal && kk > q) || kk >= kv) p = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          s = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s);
+          dp = M::mma(M::frag_direct(vtile, LD, nb * 32 * LD + ks * M::KSTEP), of[ks], dp);
         }
-        dp[e] = p * (dp[e] - dq_);
-      }
+        const bool need_mask = (causal && kb0 + 31 > qw) || (kb0 + 32 > kv);
 #pragma unroll
-      for (int c = 0; c < M::CALLS32; ++c) {
-        const typename M::frag sf = M::acc_frag(dp, c);
+        for (int e = 0; e < 16; ++e) {
+          float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
+          if (need_mask) p = (kb0 + acc_row(e, half) > lim) ? 0.f : p;
+          dp[e] = p * (dp[e] - dq_);
+        }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          acc[db] = M::mma(M::frag_trans(ktile, LD, nb * 32 * LD + db * 32, c), sf, acc[db]);
+        for (int c = 0; c < M::CALLS32; ++c) {
+          const typename M::frag sf = M::acc_frag(dp, c);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = M::mma(M::frag_trans(ktile, LD, nb * 32 * LD + db * 32, c), sf, acc[db]);
+        }
       }
+    }
+    if (kt + 1 < nkt) {
+      lds_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
+      kc.store(nxt);
+      vc.store(nxt + TILE);
+    }
+    __syncthreads();
+    if (kt + 2 < nkt) {
+      kc.load(rk, (kt + 2) * BK);
+      vc.load(rv, (kt + 2) * BK);
     }
   }
 
@@ -347,27 +391,27 @@ static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* d
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int BQ>
+template <typename T, int D, int NW, int BQ, int OCC>
 static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
   constexpr int KT = 32 * NW;
   const int TK = (p.N + KT - 1) / KT;
   const int nlog = p.B * p.H * TK;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
+  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
                      (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal, p.scale,
                      p.scale * kLog2e, p.kv_len);
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int BK>
+template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                               const float* L, const float* Dv, void* dQ, hipStream_t s) {
   constexpr int QT = 32 * NW;
   const int TQ = (p.N + QT - 1) / QT;
   const int nlog = p.B * p.H * TQ;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dq_kernel<T, D, NW, BK>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
+  hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
                      (const T*)V, (const T*)dO, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N, p.causal, p.scale,
                      p.scale * kLog2e, p.kv_len);
   return hipGetLastError();
@@ -391,7 +435,7 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                        const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
 #define X(T, DT, DD) \
-  if (dtype == DT && p.d == DD) return launch_dkdv_t<T, DD, 4, (DT == kBF16 ? 64 : 32)>(p, Q, K, V, dO, L, Dv, dK, dV, s);
+  if (dtype == DT && p.d == DD) return launch_dkdv_t<T, DD, 4, (DT == kBF16 ? 64 : 32), 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);
   ATTN_BWD_CASES(X)
 #undef X
   return hipErrorInvalidValue;
@@ -400,7 +444,7 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                      const float* L, const float* Dv, void* dQ, hipStream_t s) {
 #define X(T, DT, DD) \
-  if (dtype == DT && p.d == DD) return launch_dq_t<T, DD, 4, (DT == kBF16 ? 64 : 32)>(p, Q, K, V, dO, L, Dv, dQ, s);
+  if (dtype == DT && p.d == DD) return launch_dq_t<T, DD, 4, (DT == kBF16 ? 64 : 32), (DT == kBF16 ? 2 : 1)>(p, Q, K, V, dO, L, Dv, dQ, s);
   ATTN_BWD_CASES(X)
 #undef X
   return hipErrorInvalidValue;

@@ -25,6 +25,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) char lds_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -122,10 +123,20 @@ __device__ __forceinline__ float swap_halves(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return zero, which
+// is how rows past the end of a sequence (or past the key length) come in as zeros without a
+// branch.  Word 3 is the gfx9-family default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
 // Cooperative copy of a ROWS x COLS tile (row-major, global row stride = COLS elements) into LDS
-// with row stride LD, 16 bytes per thread per step.  Rows at or beyond `valid_rows` are zero
-// filled.  The copy is split into a register stage (load) and an LDS stage (store) so the global
-// latency can hide behind compute.
+// with row stride LD, 16 bytes per thread per step, through registers so the global latency can
+// hide behind compute.  Rows outside the resource read as zero.
 template <typename T, int ROWS, int COLS, int LD, int NTHREADS>
 struct TileCopy {
   static constexpr int CPR = COLS * (int)sizeof(T) / 16;  // 16-byte chunks per row
@@ -134,15 +145,14 @@ struct TileCopy {
   static_assert(COLS * sizeof(T) % 16 == 0, "tile rows must be a multiple of 16 bytes");
   u32x4 r[PER_THREAD];
 
-  __device__ __forceinline__ void load(const T* g, int valid_rows) {
+  // Load the tile whose first row is `row0` of the matrix behind `rs`.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       const int row = c / CPR, cc = c % CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((CHUNKS % NTHREADS == 0 || c < CHUNKS) && row < valid_rows)
-        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(g) + (size_t)row * COLS * sizeof(T) + cc * 16);
-      r[i] = v;
+      if (CHUNKS % NTHREADS == 0 || c < CHUNKS)
+        r[i] = buffer_load16(rs, (uint32_t)((row0 + row) * COLS * (int)sizeof(T) + cc * 16));
     }
   }
   __device__ __forceinline__ void store(lds_t* tile) const {
@@ -156,6 +166,21 @@ struct TileCopy {
     }
   }
 };
+
+// MFMA operand of `Mfma<T>` read straight from global memory through a buffer resource: row `row`
+// of a row-major matrix with `cols` columns, reduction columns col0.. (zero if out of range).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag_global(__amdgpu_buffer_rsrc_t rs, int row, int cols, int col0) {
+  const uint32_t off = (uint32_t)((row * cols + col0 + Mfma<T>::KPL * (lane_id() >> 5)) * (int)sizeof(T));
+  if constexpr (sizeof(T) == 2) {
+    u32x4 v = buffer_load16(rs, off);
+    typename Mfma<T>::frag f;
+    __builtin_memcpy(&f, &v, 16);
+    return f;
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0));
+  }
+}
 
 // Zero the columns [COLS, LDZ) of every row of a tile (padding read by 32-wide operand blocks
 // when the head dim is not a multiple of 32).

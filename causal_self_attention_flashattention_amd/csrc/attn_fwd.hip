@@ -24,12 +24,12 @@ namespace attn {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int NW, int BK>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                      const T* __restrict__ V, T* __restrict__ O,
-                                                      float* __restrict__ Lse, int BH, int H, int N,
-                                                      int causal, float scale_log2,
-                                                      const int32_t* __restrict__ kv_len) {
+template <typename T, int D, int NW, int BK, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                           const T* __restrict__ V, T* __restrict__ O,
+                                                           float* __restrict__ Lse, int BH, int H, int N,
+                                                           int causal, float scale_log2,
+                                                           const int32_t* __restrict__ kv_len) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int QT = 32 * NW;             // queries per workgroup
@@ -38,11 +38,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, c
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;
   constexpr int LD = DP + 16 / (int)sizeof(T);  // LDS row stride (elements), 16 bytes of pad
+  constexpr int TILE = BK * LD * (int)sizeof(T);  // bytes of one K or V tile
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BK * LD * sizeof(T)];
-  lds_t* ktile = (lds_t*)smem;
-  lds_t* vtile = ktile + BK * LD * sizeof(T);
+  // Two stages of (K tile, V tile): the next tile is written while the current one is read.
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  lds_t* lds = (lds_t*)smem;
 
   const int TQ = (N + QT - 1) / QT;
   const int logical = xcd_logical_block(BH * TQ);
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, c
   if (kv_len) kv = min(max(kv_len[b], 1), N);
 
   const size_t base = (size_t)bh * N * D;
-  Q += base; K += base; V += base; O += base;
+  O += base;
   Lse += (size_t)bh * N;
 
   const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
@@ -62,88 +63,107 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, c
   const int qw = q0 + 32 * w;  // first query of this wave
   const int q = qw + col;      // this lane's query
   const int qw_last = min(qw + 31, N - 1);
+  const bool wave_live = qw < N;
+  // Last key this lane's query may see (the mask is "key > lim").
+  const int lim = causal ? min(q, kv - 1) : kv - 1;
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
   const int nkt = (kend + BK - 1) / BK;
 
+  const auto rq = make_rsrc(Q + base, (uint32_t)(N * D * sizeof(T)));
+  const auto rk = make_rsrc(K + base, (uint32_t)(kend * D * sizeof(T)));  // keys >= kend read as 0
+  const auto rv = make_rsrc(V + base, (uint32_t)(kend * D * sizeof(T)));
+
   typename M::frag qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = M::load_global(Q + (size_t)min(q, N - 1) * D, ks * M::KSTEP, q < N);
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
 
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_part = 0.f;
 
+  if constexpr (DP > D) {
+    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + TILE);
+    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 3 * TILE);
+  }
   TileCopy<T, BK, D, LD, NT> kc, vc;
-  zero_pad_cols<T, BK, D, LD, DP, NT>(vtile);
-  kc.load(K, kend);
-  vc.load(V, kend);
+  kc.load(rk, 0);
+  vc.load(rv, 0);
+  kc.store(lds);
+  vc.store(lds + TILE);
+  __syncthreads();
+  if (nkt > 1) {
+    kc.load(rk, BK);
+    vc.load(rv, BK);
+  }
 
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    kc.store(ktile);
-    vc.store(vtile);
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      kc.load(K + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
-      vc.load(V + (size_t)(kt + 1) * BK * D, kend - (kt + 1) * BK);
-    }
+    const lds_t* ktile = lds + (kt & 1) * 2 * TILE;
+    const lds_t* vtile = ktile + TILE;
     const int k0 = kt * BK;
-    if (qw >= N || (causal && k0 > qw_last)) continue;  // no live query, or tile above the diagonal
-
-    f32x16 s[NB];
+    if (wave_live && !(causal && k0 > qw_last)) {
+      f32x16 s[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = f32x16{};
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[nb] = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
-    }
-
-    const bool need_mask = (causal && k0 + BK - 1 > qw) || (k0 + BK > kv);
-    float mx = -INFINITY;
+        for (int ks = 0; ks < KS; ++ks)
+          s[nb] = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+      }
+      // Raw scores; masked ones replaced (only on tiles that cross the diagonal or the key end).
+      if ((causal && k0 + BK - 1 > qw) || k0 + BK > kv) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[nb][e] * scale_log2;
-        if (need_mask) {
-          const int key = k0 + nb * 32 + acc_row(e, half);
-          if ((causal && key > q) || key >= kv) x = kMaskedScore;
+          for (int e = 0; e < 16; ++e)
+            s[nb][e] = (k0 + nb * 32 + acc_row(e, half) > lim) ? kMaskedScore : s[nb][e];
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = (nb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
+      mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+      if (mx > m_run + kRescaleSlack) {
+        const float alpha = fast_exp2(m_run - mx);
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        l_part *= alpha;
+        m_run = mx;
+      }
+      const float neg_m = -m_run;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, neg_m));
+          s[nb][e] = p;
+          l_part += p;
         }
-        s[nb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, swap_halves(mx));
-    if (mx > m_run + kRescaleSlack) {
-      const float alpha = fast_exp2(m_run - mx);
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-      l_part *= alpha;
-      m_run = mx;
+        for (int c = 0; c < M::CALLS32; ++c) {
+          const typename M::frag pf = M::acc_frag(s[nb], c);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
+        }
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(s[nb][e] - m_run);
-        s[nb][e] = p;
-        l_part += p;
-      }
-
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int c = 0; c < M::CALLS32; ++c) {
-        const typename M::frag pf = M::acc_frag(s[nb], c);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
-      }
+    if (kt + 1 < nkt) {
+      lds_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
+      kc.store(nxt);
+      vc.store(nxt + TILE);
+    }
+    __syncthreads();
+    if (kt + 2 < nkt) {
+      kc.load(rk, (kt + 2) * BK);
+      vc.load(rv, (kt + 2) * BK);
+    }
   }
 
   const float l_tot = l_part + swap_halves(l_part);
@@ -174,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const T* __restrict__ Q, c
   }
 }
 
-template <typename T, int D, int NW, int BK>
+template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O,
                                float* L, hipStream_t stream) {
   constexpr int QT = 32 * NW;
@@ -182,7 +202,7 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   const int nlog = p.B * p.H * TQ;
   const int grid = (nlog + 7) / 8 * 8;
   const float sl2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
                      (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len);
   return hipGetLastError();
 }
@@ -196,19 +216,19 @@ hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K,
                       float* L, hipStream_t s) {
   if (dtype == kBF16) {
     switch (p.d) {
-      case 16: return launch_fwd_t<__bf16, 16, 4, 64>(p, Q, K, V, O, L, s);
-      case 32: return launch_fwd_t<__bf16, 32, 4, 64>(p, Q, K, V, O, L, s);
-      case 64: return launch_fwd_t<__bf16, 64, 4, 64>(p, Q, K, V, O, L, s);
-      case 80: return launch_fwd_t<__bf16, 80, 4, 64>(p, Q, K, V, O, L, s);
-      case 128: return launch_fwd_t<__bf16, 128, 4, 64>(p, Q, K, V, O, L, s);
+      case 16: return launch_fwd_t<__bf16, 16, 4, 64, 2>(p, Q, K, V, O, L, s);
+      case 32: return launch_fwd_t<__bf16, 32, 4, 64, 2>(p, Q, K, V, O, L, s);
+      case 64: return launch_fwd_t<__bf16, 64, 4, 64, 2>(p, Q, K, V, O, L, s);
+      case 80: return launch_fwd_t<__bf16, 80, 4, 64, 2>(p, Q, K, V, O, L, s);
+      case 128: return launch_fwd_t<__bf16, 128, 4, 64, 2>(p, Q, K, V, O, L, s);
     }
   } else if (dtype == kF32) {
     switch (p.d) {
-      case 16: return launch_fwd_t<float, 16, 4, 32>(p, Q, K, V, O, L, s);
-      case 32: return launch_fwd_t<float, 32, 4, 32>(p, Q, K, V, O, L, s);
-      case 64: return launch_fwd_t<float, 64, 4, 32>(p, Q, K, V, O, L, s);
-      case 80: return launch_fwd_t<float, 80, 4, 32>(p, Q, K, V, O, L, s);
-      case 128: return launch_fwd_t<float, 128, 4, 32>(p, Q, K, V, O, L, s);
+      case 16: return launch_fwd_t<float, 16, 4, 32, 1>(p, Q, K, V, O, L, s);
+      case 32: return launch_fwd_t<float, 32, 4, 32, 1>(p, Q, K, V, O, L, s);
+      case 64: return launch_fwd_t<float, 64, 4, 32, 1>(p, Q, K, V, O, L, s);
+      case 80: return launch_fwd_t<float, 80, 4, 32, 1>(p, Q, K, V, O, L, s);
+      case 128: return launch_fwd_t<float, 128, 4, 32, 1>(p, Q, K, V, O, L, s);
     }
   }
   return hipErrorInvalidValue;
