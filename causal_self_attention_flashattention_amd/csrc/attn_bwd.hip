@@ -160,24 +160,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
             s = M::mma(M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP), kf[ks], s);
             dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
           }
-          const bool need_mask = (causal && kw + 31 > qb0) || (kw + 32 > kv) || (qb0 + 32 > N);
+          // Mask only blocks that cross the diagonal, the key end or the sequence end: a score
+          // whose query row is outside [qmin, N) is pushed to kMaskedScore so exp2 gives 0.
+          if ((causal && kw + 31 > qb0) || (kw + 32 > kv) || (qb0 + 32 > N)) {
+            const int lo = qmin - qb0, hi = N - qb0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int r = acc_row(e, half);
+              s[e] = (r < lo || r >= hi) ? kMaskedScore : s[e];
+            }
+          }
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const int r0 = qb * 32 + 8 * m + 4 * half;
             const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lrow + r0);
             const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + r0);
-            const float la[4] = {lv.x, lv.y, lv.z, lv.w};
-            const float da[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int e = 4 * m + r;
-              float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -la[r]));
-              if (need_mask) {
-                const int qq = q0 + r0 + r;
-                p = (qq < qmin || qq >= N) ? 0.f : p;
-              }
+              const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lv[r]));
               s[e] = p;
-              dp[e] = p * (dp[e] - da[r]);
+              dp[e] = p * (dp[e] - dd[r]);
             }
           }
 #pragma unroll
@@ -323,11 +326,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
           s = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s);
           dp = M::mma(M::frag_direct(vtile, LD, nb * 32 * LD + ks * M::KSTEP), of[ks], dp);
         }
-        const bool need_mask = (causal && kb0 + 31 > qw) || (kb0 + 32 > kv);
+        if ((causal && kb0 + 31 > qw) || (kb0 + 32 > kv)) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = (kb0 + acc_row(e, half) > lim) ? kMaskedScore : s[e];
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
-          if (need_mask) p = (kb0 + acc_row(e, half) > lim) ? 0.f : p;
+          const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
           dp[e] = p * (dp[e] - dq_);
         }
 #pragma unroll
@@ -435,7 +440,11 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                        const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
 #define X(T, DT, DD) \
-  if (dtype == DT && p.d == DD) return launch_dkdv_t<T, DD, 4, (DT == kBF16 ? 64 : 32), 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);
+  if (dtype == DT && p.d == DD) {                                                                  \
+    if (DT == kBF16 && (long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                \
+      return launch_dkdv_t<T, DD, 8, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+    return launch_dkdv_t<T, DD, 4, (DT == kBF16 ? 64 : 32), 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);   \
+  }
   ATTN_BWD_CASES(X)
 #undef X
   return hipErrorInvalidValue;
