@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
   constexpr int NQB = BQ / 32;
-  constexpr int LD = DP + 16 / (int)sizeof(T);
+  constexpr int LD = lds_pitch<T, DP>();
   constexpr int TILE = BQ * LD * (int)sizeof(T);
   constexpr int STAGE = 2 * TILE + 2 * BQ * (int)sizeof(float);  // Q tile, dO tile, L row, D row
   static_assert(2 * BQ <= NT, "one thread per staged L / D value");
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;
-  constexpr int LD = DP + 16 / (int)sizeof(T);
+  constexpr int LD = lds_pitch<T, DP>();
   constexpr int TILE = BK * LD * (int)sizeof(T);
 
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];

@@ -113,6 +113,19 @@ template <> struct Mfma<float> {
   }
 };
 
+// LDS row pitch (in elements) of a tile whose rows hold DP elements of T.  Two read patterns touch
+// these tiles: 16-byte-per-lane reads of 32 consecutive rows (operands whose reduction runs along a
+// row) and 8-byte transposing reads of 4-row x 16-column blocks.  Measured on gfx950, the first
+// runs at full rate only when the pitch is 16 bytes modulo 32, and the second drops to half rate
+// when the pitch is within 16 bytes of a multiple of 256; the pitch below satisfies both.
+template <typename T, int DP>
+constexpr int lds_pitch() {
+  int bytes = DP * (int)sizeof(T) + 16;
+  const int m = bytes % 256;
+  if (m == 0 || m == 16 || m == 240) bytes += 32;
+  return bytes / (int)sizeof(T);
+}
+
 // Exchange a value with the lane 32 positions away (lanes l and l ^ 32 hold the two halves of
 // an accumulator column).
 __device__ __forceinline__ float swap_halves(float x) {

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;
-  constexpr int LD = DP + 16 / (int)sizeof(T);  // LDS row stride (elements), 16 bytes of pad
+  constexpr int LD = lds_pitch<T, DP>();  // LDS row stride (elements)
   constexpr int TILE = BK * LD * (int)sizeof(T);  // bytes of one K or V tile
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
 
