@@ -112,6 +112,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
       kf[ks] = frag_global<T>(rk, key, D, ks * M::KSTEP);
       vf[ks] = frag_global<T>(rv, key, D, ks * M::KSTEP);
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      settle(kf[ks]);
+      settle(vf[ks]);
+    }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
     const int nqt = TQ - qt0;
@@ -123,19 +128,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
       zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + STAGE + TILE);
     }
     TileCopy<T, BQ, D, LD, NT> qc, oc;
-    float lrd = 0.f;  // one staged L*log2(e) (threads < BQ) or D (threads BQ..2BQ-1) value
+    // One staged value per thread: L (threads < BQ) or D (threads BQ..2BQ-1).  L is scaled to
+    // log2 units only when it is written to LDS, so that no arithmetic waits on the load here.
+    float lrd = 0.f;
     auto load_stage = [&](int qt) {
       qc.load(rq, qt * BQ);
       oc.load(ro, qt * BQ);
       const int t = threadIdx.x;
-      if (t < BQ) lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (qt * BQ + t) * 4, 0, 0)) * kLog2e;
-      else if (t < 2 * BQ) lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (qt * BQ + t - BQ) * 4, 0, 0));
+      if (t < 2 * BQ)
+        lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t < BQ ? rl : rd, (qt * BQ + (t % BQ)) * 4, 0, 0));
     };
     auto store_stage = [&](lds_t* st) {
       qc.store(st);
       oc.store(st + TILE);
       if (threadIdx.x < 2 * BQ)
-        reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] = lrd;
+        reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
+            threadIdx.x < BQ ? lrd * kLog2e : lrd;
     };
     load_stage(qt0);
     store_stage(lds);
@@ -293,6 +301,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : 0.f;
   const float dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(qf[ks]);
+    settle(of[ks]);
+  }
+  settle(lq);
+  settle(dq_);
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -437,23 +452,34 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
   return hipErrorInvalidValue;
 }
 
+// Tile choices (measured on MI355X): for bf16 head dims up to 80, two 4-wave workgroups per CU with
+// 64-query stages (waves of different workgroups share a SIMD, so their MFMA and VALU phases
+// interleave); at d = 128 the register file only holds 2 waves per SIMD, so one 8-wave workgroup
+// with 32-query stages for large grids.
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                        const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
-    if (DT == kBF16 && (long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                \
+    if (DT == kF32) return launch_dkdv_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);        \
+    if (DD <= 80) return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s);          \
+    if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                               \
       return launch_dkdv_t<T, DD, 8, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
-    return launch_dkdv_t<T, DD, 4, (DT == kBF16 ? 64 : 32), 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);   \
+    return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                        \
   }
   ATTN_BWD_CASES(X)
 #undef X
   return hipErrorInvalidValue;
 }
 
+// dQ: 4-wave workgroups, two per CU; key tiles of 32 for head dims up to 80, 64 at d = 128.
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                      const float* L, const float* Dv, void* dQ, hipStream_t s) {
 #define X(T, DT, DD) \
-  if (dtype == DT && p.d == DD) return launch_dq_t<T, DD, 4, (DT == kBF16 ? 64 : 32), (DT == kBF16 ? 2 : 1)>(p, Q, K, V, dO, L, Dv, dQ, s);
+  if (dtype == DT && p.d == DD) {                                                                  \
+    if (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dQ, s);              \
+    if (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, L, Dv, dQ, s);                \
+    return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dQ, s);                              \
+  }
   ATTN_BWD_CASES(X)
 #undef X
   return hipErrorInvalidValue;

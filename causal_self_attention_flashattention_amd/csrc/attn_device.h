@@ -208,6 +208,13 @@ __device__ __forceinline__ void zero_pad_cols(lds_t* tile) {
   }
 }
 
+// Wait, outside any loop, until registers filled by global loads have arrived.  Without it the
+// compiler may place the vector-memory wait for them inside the following loop, where in-order
+// counting makes it also wait for every tile prefetch issued since -- exposing a full memory
+// latency per iteration.
+template <typename F>
+__device__ __forceinline__ void settle(const F& f) { asm volatile("" ::"v"(f)); }
+
 // Block index -> logical work item, so that the 8 XCDs (which receive workgroups round-robin)
 // each get a contiguous range of logical items, i.e. whole heads, and share that head's K/V in
 // their own L2.  The grid is padded to a multiple of 8; padding blocks get -1.

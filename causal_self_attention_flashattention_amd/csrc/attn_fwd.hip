@@ -78,6 +78,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   typename M::frag qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
   f32x16 o[NDB];
 #pragma unroll
