@@ -26,7 +26,7 @@ SIGNATURES = {
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "attn_bwd_rowdot": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
     "attn_version": (_i, []),
@@ -158,14 +158,17 @@ def bwd_dkdv(q, k, v, do, lse, D, causal: bool = True, scale: float | None = Non
     return dk, dv
 
 
-def bwd_dq(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None, kv_len=None, out=None):
-    """dQ alone (the backward's third step), given L and D."""
+def bwd_dq(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None, kv_len=None, out=None, o=None):
+    """dQ alone, given L.  With ``o`` (the forward output) the kernel also computes D = rowsum(O o dO)
+    into ``D`` (an output then); without it ``D`` is an input.  Returns dQ."""
     B, H, N, d = _check_qkv(q, k, v, do)
+    if o is not None:
+        _check_qkv(q, o)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if out is None else out
     kv = _kv_tensor(kv_len, B, q.device)
-    st = load_library().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dq), B, H, N, d,
-                                    int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
+    st = load_library().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o), _ptr(lse), _ptr(D), _ptr(dq), B, H,
+                                    N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
     _check("attn_bwd_dq", st)
     return dq
 

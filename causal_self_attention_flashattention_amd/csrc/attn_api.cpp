@@ -122,9 +122,10 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
   const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len};
-  if (attn::launch_rowdot(dtype, p, O, dO, D, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  // The dQ kernel computes D for its query rows on the way (replacing the separate pre-pass), so it
+  // runs first; the dK/dV kernel then reads D.
+  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
   if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream) != hipSuccess) return ATTN_E_LAUNCH;
-  if (attn::launch_dq(dtype, p, Q, K, V, dO, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
   return ATTN_OK;
 }
 
@@ -149,24 +150,28 @@ int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, c
   return ATTN_OK;
 }
 
-int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
-                void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype, const int32_t* kv_len,
-                hipStream_t stream) {
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const void* O, const float* L,
+                float* D, void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype,
+                const int32_t* kv_len, hipStream_t stream) {
   if (!Q || !K || !V || !dO || !L || !D || !dQ) return ATTN_E_NULL;
   int st = check_common(B, H, N, d, dtype, scale, true);
   if (st != ATTN_OK) return st;
   const void* ptrs[] = {Q, K, V, dO, L, D, dQ};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_E_ALIGN;
+  if (O && !aligned16(O)) return ATTN_E_ALIGN;
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
   const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range outs[1] = {range_of(dQ, tb)};
+  // D is an output when O is given, an input otherwise.
+  const Range outs[2] = {range_of(dQ, tb), range_of(D, lb)};
   const Range ins[7] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(dO, tb),
-                        range_of(L, lb), range_of(D, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}};
-  st = check_alias(outs, 1, ins, 7);
+                        range_of(L, lb), O ? range_of(O, tb) : Range{0, 0},
+                        kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}};
+  st = O ? check_alias(outs, 2, ins, 7) : check_alias(outs, 1, ins, 7);
   if (st != ATTN_OK) return st;
+  if (!O && overlap(outs[0], outs[1])) return ATTN_E_ALIAS;
   const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len};
-  if (attn::launch_dq(dtype, p, Q, K, V, dO, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
   return ATTN_OK;
 }
 

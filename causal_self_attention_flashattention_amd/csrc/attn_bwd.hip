@@ -27,26 +27,24 @@ namespace attn {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                      float* __restrict__ Dv, int rows) {
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;              // chunks per row
-  constexpr int TPR = CPR <= 1 ? 1 : CPR <= 2 ? 2 : CPR <= 4 ? 4 : CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;
-  static_assert(D % EPC == 0 && CPR <= 32, "unsupported head dim");
-  constexpr int RPB = 256 / TPR;  // rows per block per step
-  const int sub = threadIdx.x % TPR;
-  for (int row = blockIdx.x * RPB + threadIdx.x / TPR; row < rows; row += gridDim.x * RPB) {
-    float acc = 0.f;
-    if (sub < CPR) {
-      const uint4 a = *reinterpret_cast<const uint4*>(O + (size_t)row * D + sub * EPC);
-      const uint4 g = *reinterpret_cast<const uint4*>(dO + (size_t)row * D + sub * EPC);
-      T av[EPC], gv[EPC];
-      __builtin_memcpy(av, &a, 16);
-      __builtin_memcpy(gv, &g, 16);
+  // Thread pair (2i, 2i+1) owns row i; thread `half` of the pair reduces the columns an MFMA operand
+  // fragment of that half holds (fragments ks = 0.. in order), then the two halves are added.
+  using M = Mfma<T>;
+  constexpr int KS = D / M::KSTEP;
+  const int half = threadIdx.x & 1;
+  for (int row = (blockIdx.x * 256 + threadIdx.x) >> 1; row < rows; row += gridDim.x * 128) {
+    const T* orow = O + (size_t)row * D + M::KPL * half;
+    const T* grow = dO + (size_t)row * D + M::KPL * half;
+    float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) acc += (float)av[i] * (float)gv[i];
+    for (int ks = 0; ks < KS; ++ks) {
+      typename M::frag a, g;
+      __builtin_memcpy(&a, orow + ks * M::KSTEP, sizeof(a));
+      __builtin_memcpy(&g, grow + ks * M::KSTEP, sizeof(g));
+      part = frag_dot(a, g, part);
     }
-#pragma unroll
-    for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
-    if (sub == 0) Dv[row] = acc;
+    const float other = __shfl_xor(part, 1, 2);
+    if (half == 0) Dv[row] = part + other;
   }
 }
 
@@ -248,8 +246,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
 template <typename T, int D, int NW, int BK, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dQ, int BH, int H, int N,
-    int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+    const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
+    int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+  // With Oin != nullptr the kernel first computes D = rowsum(O o dO) for its own query rows (each
+  // row belongs to exactly one workgroup) and stores it to Dv for the dK/dV kernel that follows;
+  // otherwise it reads D from Dv.
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int QT = 32 * NW;
@@ -300,7 +301,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
     of[ks] = frag_global<T>(ro, q, D, ks * M::KSTEP);
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : 0.f;
-  const float dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+  float dq_;
+  if (Oin) {
+    const auto rO = make_rsrc(Oin + base, tbytes);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) part = frag_dot(frag_global<T>(rO, q, D, ks * M::KSTEP), of[ks], part);
+    dq_ = part + swap_halves(part);
+    if (half == 0 && q < N) Dv[(size_t)bh * N + q] = dq_;
+  } else {
+    dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+  }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(qf[ks]);
@@ -402,10 +413,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
 template <typename T, int D>
 static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* dO, float* Dv, hipStream_t s) {
   const int rows = p.B * p.H * p.N;
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int TPR = CPR <= 1 ? 1 : CPR <= 2 ? 2 : CPR <= 4 ? 4 : CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;
-  constexpr int RPB = 256 / TPR;
-  int grid = (rows + RPB - 1) / RPB;
+  int grid = (rows + 127) / 128;  // 128 rows per 256-thread block
   if (grid > 256 * 16) grid = 256 * 16;
   hipLaunchKernelGGL((rowdot_kernel<T, D>), dim3(grid), dim3(256), 0, s, (const T*)O, (const T*)dO, Dv, rows);
   return hipGetLastError();
@@ -426,14 +434,14 @@ static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, 
 
 template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                              const float* L, const float* Dv, void* dQ, hipStream_t s) {
+                              const void* O, const float* L, float* Dv, void* dQ, hipStream_t s) {
   constexpr int QT = 32 * NW;
   const int TQ = (p.N + QT - 1) / QT;
   const int nlog = p.B * p.H * TQ;
   const int grid = (nlog + 7) / 8 * 8;
   hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
-                     (const T*)V, (const T*)dO, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N, p.causal, p.scale,
-                     p.scale * kLog2e, p.kv_len);
+                     (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N, p.causal,
+                     p.scale, p.scale * kLog2e, p.kv_len);
   return hipGetLastError();
 }
 
@@ -473,12 +481,12 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
 
 // dQ: 4-wave workgroups, two per CU; key tiles of 32 for head dims up to 80, 64 at d = 128.
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                     const float* L, const float* Dv, void* dQ, hipStream_t s) {
+                     const void* O, const float* L, float* Dv, void* dQ, hipStream_t s) {
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
-    if (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dQ, s);              \
-    if (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, L, Dv, dQ, s);                \
-    return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dQ, s);                              \
+    if (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s);           \
+    if (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);             \
+    return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);                           \
   }
   ATTN_BWD_CASES(X)
 #undef X

@@ -195,6 +195,16 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_global(__amdgpu_buffer_rs
   }
 }
 
+// Sum of elementwise products of two MFMA operand fragments, in fp32 with one fused multiply-add
+// per element in fragment order.  The D pre-pass and the dQ kernel both reduce a row of O o dO with
+// it, fragment by fragment in the same order, so their D values agree bitwise.
+__device__ __forceinline__ float frag_dot(const bf16x8& a, const bf16x8& b, float acc) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = __builtin_fmaf((float)a[t], (float)b[t], acc);
+  return acc;
+}
+__device__ __forceinline__ float frag_dot(float a, float b, float acc) { return __builtin_fmaf(a, b, acc); }
+
 // Zero the columns [COLS, LDZ) of every row of a tile (padding read by 32-wide operand blocks
 // when the head dim is not a multiple of 32).
 template <typename T, int ROWS, int COLS, int LD, int LDZ, int NTHREADS>

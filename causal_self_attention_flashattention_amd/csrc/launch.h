@@ -30,7 +30,9 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
                        const void* dO, const float* L, const float* Dv, void* dK, void* dV,
                        hipStream_t stream);
 
+// dQ; with O != nullptr it also computes D = rowsum(O o dO) for its rows and stores it to Dv
+// (which is then an output), else it reads D from Dv.
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
-                     const void* dO, const float* L, const float* Dv, void* dQ, hipStream_t stream);
+                     const void* dO, const void* O, const float* L, float* Dv, void* dQ, hipStream_t stream);
 
 }  // namespace attn

@@ -85,11 +85,16 @@ int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, c
                   void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, int dtype,
                   const int32_t* kv_len, hipStream_t stream);
 
-/* The backward's third step alone: dQ for every query tile (eqs. 13-14, 16-18 of the handout,
- * §4.1), P recomputed a second time so that no two workgroups write the same output. */
-int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
-                void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype, const int32_t* kv_len,
-                hipStream_t stream);
+/* dQ for every query tile (eqs. 13-14, 16-18 of the handout's §4.2.2), P recomputed a second time
+ * so that no two workgroups write the same output (§4.2.3).
+ *   O   in, optional: [B,H,N,d] dtype forward output.  When non-NULL the kernel first computes
+ *       D = rowsum(O o dO) for its own query rows and writes it to D (D is then an output, and this
+ *       call replaces attn_bwd_rowdot); when NULL, D is an input (from attn_bwd_rowdot).
+ *   D   [B,H,N] float32, see O.
+ * attn_bwd = attn_bwd_dq with O, then attn_bwd_dkdv.  Other arguments as for attn_bwd. */
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const void* O, const float* L,
+                float* D, void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype,
+                const int32_t* kv_len, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -113,6 +113,25 @@ def test_rowdot_rejects_bad_arguments(lib):
     assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 16, 64, 3, None) == E_DTYPE
 
 
+def _dq(lib, **kw):
+    p = dict(Q=A, K=A + SZ, V=A + 2 * SZ, dO=A + 3 * SZ, O=A + 4 * SZ, L=A + 5 * SZ, D=A + 6 * SZ, dQ=A + 7 * SZ,
+             B=1, H=1, N=16, d=64, causal=1, scale=0.125, dtype=1, kv=None)
+    p.update(kw)
+    return lib.attn_bwd_dq(p["Q"], p["K"], p["V"], p["dO"], p["O"], p["L"], p["D"], p["dQ"], p["B"], p["H"], p["N"],
+                           p["d"], p["causal"], p["scale"], p["dtype"], p["kv"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=None), E_NULL), (dict(L=None), E_NULL), (dict(dQ=None), E_NULL),
+    (dict(d=48), E_HEADDIM), (dict(O=A + 4 * SZ + 8), E_ALIGN),
+    (dict(D=A + 4 * SZ + 64), E_ALIAS),   # D (an output when O is given) inside O
+    (dict(dQ=A + 3 * SZ), E_ALIAS),       # dQ == dO
+    (dict(O=None, D=A + 7 * SZ + 32), E_ALIAS),  # D (input) overlapping dQ
+])
+def test_dq_rejects_bad_arguments(lib, kw, status):
+    assert _dq(lib, **kw) == status
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 4, 64)

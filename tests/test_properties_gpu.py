@@ -102,9 +102,11 @@ def test_causality_is_bitwise():
     assert not torch.equal(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 80), ("f32", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 80), ("bf16", 128), ("f32", 128)])
 def test_deterministic_and_substeps_equal_bwd(dtype, d):
-    """Two runs are bitwise equal (no atomics), and attn_bwd == rowdot, then dK/dV, then dQ."""
+    """Two runs are bitwise equal (no atomics); attn_bwd equals its steps run one by one (dQ computing
+    D, then dK/dV); the stand-alone D pre-pass gives the same D bitwise, and dQ fed with it gives the
+    same dQ."""
     require_gpu()
     B, H, N = 2, 3, 517
     announce(f"determinism dtype={dtype} d={d}")
@@ -116,12 +118,16 @@ def test_deterministic_and_substeps_equal_bwd(dtype, d):
     for t1, t2 in zip(*runs):
         assert torch.equal(t1, t2)
     o, L = runs[0][:2]
-    D = attn.rowdot(o, x["do"])
+    D = torch.empty_like(L)
+    dq = attn.bwd_dq(x["q"], x["k"], x["v"], x["do"], L, D, causal=True, kv_len=x["kv_len"], o=o)
     dk, dv = attn.bwd_dkdv(x["q"], x["k"], x["v"], x["do"], L, D, causal=True, kv_len=x["kv_len"])
-    dq = attn.bwd_dq(x["q"], x["k"], x["v"], x["do"], L, D, causal=True, kv_len=x["kv_len"])
+    D2 = attn.rowdot(o, x["do"])
+    dq2 = attn.bwd_dq(x["q"], x["k"], x["v"], x["do"], L, D2, causal=True, kv_len=x["kv_len"])
     torch.cuda.synchronize()
     for got, want in zip((dq, dk, dv, D), runs[0][2:]):
         assert torch.equal(got, want)
+    assert torch.equal(D2, D)
+    assert torch.equal(dq2, dq)
 
 
 def _guarded(shape, dtype, pad_elems=4096):
