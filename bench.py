@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: causal attention forward + backward on one MI355X, through the C ABI.
 
-One step = the whole path over one batch: attn_fwd, then the backward's two kernels
-(attn_bwd_dq, which also computes D = rowsum(O o dO), then attn_bwd_dkdv -- exactly what attn_bwd
-launches), on torch's current HIP stream, with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
+One step = the whole path over one batch: attn_fwd, then the backward exactly as attn_bwd launches it
+-- either its two kernels called one by one (attn_bwd_dq, which also computes D = rowsum(O o dO),
+then attn_bwd_dkdv) or, for small problems, attn_bwd itself, whose dQ and dK/dV work share one
+launch -- on torch's current HIP stream, with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
 bracketed by torch.cuda.synchronize(); HIP events recorded on the same stream between the kernels
 give each kernel's average duration.  Prints one JSON line.
 
@@ -32,7 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16 MFM
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "gpt2-small"
-KERNELS = ("fwd", "dq", "dkdv")  # launch order of one step
+KERNELS_SPLIT = ("fwd", "dq", "dkdv")  # launch order of one step when attn_bwd launches two kernels
+KERNELS_FUSED = ("fwd", "bwd")        # ... and when its dQ and dK/dV work share one launch
 KERNEL_SOURCES = ("attn_device.h", "attn_fwd.hip", "attn_bwd.hip")
 
 
@@ -53,6 +55,7 @@ def kernel_work(w, kv: int) -> dict:
         "fwd": ("flop", 4 * d * P * BH),
         "dkdv": ("flop", 8 * d * P * BH),   # S, dP, dV, dK
         "dq": ("flop", 2 * d * P * BH),     # dQ (its recompute of S and dP, and D, are not credited)
+        "bwd": ("flop", 10 * d * P * BH),   # dQ and dK/dV in one launch
     }
 
 
@@ -185,8 +188,10 @@ def main():
 
     def step_binding():
         attn.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_len=kvd, out=o, lse=L)
-        attn.bwd_dq(q, k, v, do, L, D, causal=w.causal, scale=w.scale, kv_len=kvd, out=dq, o=o)
-        attn.bwd_dkdv(q, k, v, do, L, D, causal=w.causal, scale=w.scale, kv_len=kvd, outs=(dk, dv))
+        attn.bwd(q, k, v, o, do, L, causal=w.causal, scale=w.scale, kv_len=kvd, outs=(dq, dk, dv, D))
+
+    fused = attn.bwd_launches(B, H, N, d, q.dtype) == 1
+    KERNELS = KERNELS_FUSED if fused else KERNELS_SPLIT
 
     def step(ev=None):
         rec = hip.hipEventRecord
@@ -195,14 +200,20 @@ def main():
         st = lib.attn_fwd(P_["q"], P_["k"], P_["v"], P_["o"], P_["L"], B, H, N, d, c, sc, dt, kvp, stream)
         if ev is not None:
             rec(ev[1], stream)
-        st |= lib.attn_bwd_dq(P_["q"], P_["k"], P_["v"], P_["do"], P_["o"], P_["L"], P_["D"], P_["dq"], B, H, N, d,
-                              c, sc, dt, kvp, stream)
-        if ev is not None:
-            rec(ev[2], stream)
-        st |= lib.attn_bwd_dkdv(P_["q"], P_["k"], P_["v"], P_["do"], P_["L"], P_["D"], P_["dk"], P_["dv"], B, H, N,
-                                d, c, sc, dt, kvp, stream)
-        if ev is not None:
-            rec(ev[3], stream)
+        if fused:
+            st |= lib.attn_bwd(P_["q"], P_["k"], P_["v"], P_["o"], P_["do"], P_["L"], P_["dq"], P_["dk"], P_["dv"],
+                               P_["D"], B, H, N, d, c, sc, dt, kvp, stream)
+            if ev is not None:
+                rec(ev[2], stream)
+        else:
+            st |= lib.attn_bwd_dq(P_["q"], P_["k"], P_["v"], P_["do"], P_["o"], P_["L"], P_["D"], P_["dq"], B, H, N,
+                                  d, c, sc, dt, kvp, stream)
+            if ev is not None:
+                rec(ev[2], stream)
+            st |= lib.attn_bwd_dkdv(P_["q"], P_["k"], P_["v"], P_["do"], P_["L"], P_["D"], P_["dk"], P_["dv"], B, H,
+                                    N, d, c, sc, dt, kvp, stream)
+            if ev is not None:
+                rec(ev[3], stream)
         if st != 0:
             raise RuntimeError(f"attention step failed with status {st}")
 

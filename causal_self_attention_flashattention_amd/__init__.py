@@ -7,6 +7,7 @@ The computation lives in ``libattn.so`` (HIP kernels for gfx950 behind a C ABI, 
 from .binding import (  # noqa: F401
     AttnError,
     bwd,
+    bwd_launches,
     bwd_dkdv,
     bwd_dq,
     fwd,
@@ -16,4 +17,4 @@ from .binding import (  # noqa: F401
     supported,
 )
 
-__all__ = ["fwd", "bwd", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]
+__all__ = ["fwd", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

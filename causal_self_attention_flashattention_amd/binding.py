@@ -29,6 +29,7 @@ SIGNATURES = {
     "attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
+    "attn_bwd_launches": (_i, [_i, _i, _i, _i, _i]),
     "attn_version": (_i, []),
 }
 
@@ -171,6 +172,14 @@ def bwd_dq(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None,
                                     N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
     _check("attn_bwd_dq", st)
     return dq
+
+
+def bwd_launches(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Number of kernels attn_bwd launches for this problem (1: dQ and dK/dV share one launch)."""
+    n = load_library().attn_bwd_launches(int(B), int(H), int(N), int(d), _DTYPES[dtype])
+    if n < 0:
+        raise AttnError("attn_bwd_launches", n, status_string(n))
+    return n
 
 
 def supported(dtype, d: int) -> bool:

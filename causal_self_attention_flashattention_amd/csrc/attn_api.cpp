@@ -51,6 +51,13 @@ extern "C" {
 
 int attn_version(void) { return 10000; }
 
+int attn_bwd_launches(int B, int H, int N, int d, int dtype) {
+  const int st = check_common(B, H, N, d, dtype, 1.0f, false);
+  if (st != ATTN_OK) return st;
+  const attn::Problem p{B, H, N, d, 1, 1.0f, nullptr};
+  return attn::bwd_small_applies(dtype, p) ? 1 : 2;
+}
+
 int attn_supported(int dtype, int d) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return 0;
   return attn::fwd_supported(dtype, d) && attn::bwd_supported(dtype, d) ? 1 : 0;
@@ -122,6 +129,12 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   st = check_alias(outs, 4, ins, 7);
   if (st != ATTN_OK) return st;
   const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len};
+  if (attn::bwd_small_applies(dtype, p)) {
+    // Small grids: dQ and dK/dV side by side in one launch.
+    if (attn::launch_bwd_small(dtype, p, Q, K, V, dO, O, L, D, dQ, dK, dV, stream) != hipSuccess)
+      return ATTN_E_LAUNCH;
+    return ATTN_OK;
+  }
   // The dQ kernel computes D for its query rows on the way (replacing the separate pre-pass), so it
   // runs first; the dK/dV kernel then reads D.
   if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;

@@ -52,11 +52,29 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 // dK, dV: one workgroup per (head, 32*NW keys); loop over query tiles of BQ rows, double
 // buffered in LDS together with the tile's L*log2(e) and D values.
 
-template <typename T, int D, int NW, int BQ, int OCC>
-__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
-    int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+// LDS bytes of the dK/dV body: two stages of (Q tile, dO tile, L row, D row), then either (DSELF)
+// one float of D per query row for rows up to kDselfMaxN, or (VLDS) the workgroup's V rows.
+constexpr int kDselfMaxN = 4096;
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS>
+constexpr int dkdv_lds_bytes() {
+  constexpr int DP = (D + 31) / 32 * 32;
+  constexpr int TILE = BQ * lds_pitch<T, DP>() * (int)sizeof(T);
+  return 2 * (2 * TILE + 2 * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
+         (VLDS ? 32 * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0);
+}
+
+// One dK/dV work item (logical block `block` of the grid described by BH, N).  With DSELF the body
+// does not read D: it first computes D = rowsum(O o dO) for every query row it will visit, in the
+// same fragment order as the D pre-pass, into LDS (requires N <= kDselfMaxN).  With VLDS the
+// workgroup's V rows are kept in LDS and read per block instead of being held in registers (frees
+// 32 VGPRs per wave at d = 128, where the register file is otherwise too small for two waves per
+// SIMD without spilling).
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS>
+__device__ __forceinline__ void dkdv_body(
+    char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
+    const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal,
+    float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int KT = 32 * NW;  // keys per workgroup
@@ -69,11 +87,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
   constexpr int STAGE = 2 * TILE + 2 * BQ * (int)sizeof(float);  // Q tile, dO tile, L row, D row
   static_assert(2 * BQ <= NT, "one thread per staged L / D value");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   lds_t* lds = (lds_t*)smem;
 
   const int TK = (N + KT - 1) / KT;
-  const int logical = xcd_logical_block(BH * TK);
+  const int logical = xcd_logical_block(BH * TK, block);
   if (logical < 0) return;
   const int bh = logical / TK;
   const int kt = logical % TK;  // low key tiles see the most queries under causal masking
@@ -104,20 +121,48 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
     const auto ro = make_rsrc(dO + base, tbytes);
     const auto rl = make_rsrc(Lse + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
     const auto rd = make_rsrc(Dv + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
-    typename M::frag kf[KS], vf[KS];
+    typename M::frag kf[KS], vf[VLDS ? 1 : KS];
+    lds_t* vt = lds + 2 * STAGE;  // VLDS: V rows k0 .. k0 + KT - 1
+    if constexpr (VLDS) {
+      TileCopy<T, KT, D, LD, NT> vcp;
+      vcp.load(rv, k0);
+      vcp.store(vt);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = frag_global<T>(rk, key, D, ks * M::KSTEP);
-      vf[ks] = frag_global<T>(rv, key, D, ks * M::KSTEP);
+      if constexpr (!VLDS) vf[ks] = frag_global<T>(rv, key, D, ks * M::KSTEP);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       settle(kf[ks]);
-      settle(vf[ks]);
+      if constexpr (!VLDS) settle(vf[ks]);
     }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
     const int nqt = TQ - qt0;
+
+    // DSELF: D for rows [qt0*BQ, N), one row per thread at a time, kept in LDS after the stages.
+    __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
+    if constexpr (DSELF) {
+      for (int r = qt0 * BQ + threadIdx.x; r < N; r += NT) {
+        const T* orow = Oin + base + (size_t)r * D;
+        const T* grow = dO + base + (size_t)r * D;
+        float part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          part[h] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            typename M::frag a, g;
+            __builtin_memcpy(&a, orow + ks * M::KSTEP + M::KPL * h, sizeof(a));
+            __builtin_memcpy(&g, grow + ks * M::KSTEP + M::KPL * h, sizeof(g));
+            part[h] = frag_dot(a, g, part[h]);
+          }
+        }
+        dself[r - qt0 * BQ] = part[0] + part[1];
+      }
+    }
 
     if constexpr (DP > D) {
       zero_pad_cols<T, BQ, D, LD, DP, NT>(lds);
@@ -133,13 +178,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
       qc.load(rq, qt * BQ);
       oc.load(ro, qt * BQ);
       const int t = threadIdx.x;
-      if (t < 2 * BQ)
+      if (t < (DSELF ? BQ : 2 * BQ))
         lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t < BQ ? rl : rd, (qt * BQ + (t % BQ)) * 4, 0, 0));
     };
     auto store_stage = [&](lds_t* st) {
       qc.store(st);
       oc.store(st + TILE);
-      if (threadIdx.x < 2 * BQ)
+      if (threadIdx.x < (DSELF ? BQ : 2 * BQ))
         reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
             threadIdx.x < BQ ? lrd * kLog2e : lrd;
     };
@@ -154,7 +199,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
       const lds_t* otile = qtile + TILE;
       const __attribute__((address_space(3))) float* lrow =
           reinterpret_cast<const __attribute__((address_space(3))) float*>(qtile + 2 * TILE);
-      const __attribute__((address_space(3))) float* drow = lrow + BQ;
+      const __attribute__((address_space(3))) float* drow = DSELF ? dself + it * BQ : lrow + BQ;
       if (wave_live) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -164,7 +209,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             s = M::mma(M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP), kf[ks], s);
-            dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
+            if constexpr (VLDS)
+              dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP),
+                          M::frag_direct(vt, LD, w * 32 * LD + ks * M::KSTEP), dp);
+            else
+              dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
           }
           // Mask only blocks that cross the diagonal, the key end or the sequence end: a score
           // whose query row is outside [qmin, N) is pushed to kMaskedScore so exp2 gives 0.
@@ -240,14 +289,31 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
   }
 }
 
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS>
+__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
+    int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS>()];
+  dkdv_body<T, D, NW, BQ, false, VLDS>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N, causal,
+                                       scale, scale_log2, kv_len);
+}
+
 // ------------------------------------------------------------------------------------------
 // dQ: one workgroup per (head, 32*NW queries); loop over key tiles of BK rows, double buffered.
 
-template <typename T, int D, int NW, int BK, int OCC>
-__global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
-    int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+template <typename T, int D, int BK>
+constexpr int dq_lds_bytes() {
+  constexpr int DP = (D + 31) / 32 * 32;
+  return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T);
+}
+
+template <typename T, int D, int NW, int BK>
+__device__ __forceinline__ void dq_body(
+    char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
+    T* __restrict__ dQ, int BH, int H, int N, int causal, float scale, float scale_log2,
+    const int32_t* __restrict__ kv_len) {
   // With Oin != nullptr the kernel first computes D = rowsum(O o dO) for its own query rows (each
   // row belongs to exactly one workgroup) and stores it to Dv for the dK/dV kernel that follows;
   // otherwise it reads D from Dv.
@@ -261,11 +327,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
   constexpr int LD = lds_pitch<T, DP>();
   constexpr int TILE = BK * LD * (int)sizeof(T);
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
   lds_t* lds = (lds_t*)smem;
 
   const int TQ = (N + QT - 1) / QT;
-  const int logical = xcd_logical_block(BH * TQ);
+  const int logical = xcd_logical_block(BH * TQ, block);
   if (logical < 0) return;
   const int bh = logical / TQ;
   const int qt = TQ - 1 - logical % TQ;
@@ -407,6 +472,36 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
   }
 }
 
+template <typename T, int D, int NW, int BK, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
+    int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, BK>()];
+  dq_body<T, D, NW, BK>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2, kv_len);
+}
+
+// ------------------------------------------------------------------------------------------
+// Small problems: dQ and dK/dV in one launch.  The first nq blocks run dQ work items (which also
+// store D), the rest run dK/dV work items that compute D themselves, so the two halves have no
+// ordering between them and run side by side when the grid would otherwise leave CUs idle.
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_small_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ O, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ,
+    T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal, float scale, float scale_log2,
+    const int32_t* __restrict__ kv_len, int nq) {
+  __shared__ __attribute__((aligned(16))) char smem[cmax(dq_lds_bytes<T, D, 32>(), dkdv_lds_bytes<T, D, 4, 64, true, false>())];
+  if ((int)blockIdx.x < nq)
+    dq_body<T, D, 4, 32>(smem, blockIdx.x, Q, K, V, dO, O, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2, kv_len);
+  else
+    dkdv_body<T, D, 4, 64, true, false>(smem, blockIdx.x - nq, Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal, scale,
+                                 scale_log2, kv_len);
+}
+
 // ------------------------------------------------------------------------------------------
 // launchers
 
@@ -419,14 +514,14 @@ static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* d
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int BQ, int OCC>
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS = false>
 static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
   constexpr int KT = 32 * NW;
   const int TK = (p.N + KT - 1) / KT;
   const int nlog = p.B * p.H * TK;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
+  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
                      (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal, p.scale,
                      p.scale * kLog2e, p.kv_len);
   return hipGetLastError();
@@ -447,6 +542,37 @@ static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, co
 
 bool bwd_supported(int dtype, int d) { return fwd_supported(dtype, d); }
 
+template <typename T, int D>
+static hipError_t launch_bwd_small_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                                     const void* O, const float* L, float* Dv, void* dQ, void* dK, void* dV,
+                                     hipStream_t s) {
+  const int BH = p.B * p.H;
+  const int nq = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
+  const int nk = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
+  hipLaunchKernelGGL((bwd_small_kernel<T, D>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
+                     (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
+                     p.scale, p.scale * kLog2e, p.kv_len, nq);
+  return hipGetLastError();
+}
+
+bool bwd_small_applies(int dtype, const Problem& p) {
+  if (dtype != kBF16 || p.d > 80 || p.N > kDselfMaxN) return false;
+  // both halves together fit in one pass of two 4-wave workgroups per CU
+  return 2L * p.B * p.H * ((p.N + 127) / 128) <= 512;
+}
+
+hipError_t launch_bwd_small(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                            const void* O, const float* L, float* Dv, void* dQ, void* dK, void* dV, hipStream_t s) {
+  if (!bwd_small_applies(dtype, p)) return hipErrorInvalidValue;
+  switch (p.d) {
+    case 16: return launch_bwd_small_t<__bf16, 16>(p, Q, K, V, dO, O, L, Dv, dQ, dK, dV, s);
+    case 32: return launch_bwd_small_t<__bf16, 32>(p, Q, K, V, dO, O, L, Dv, dQ, dK, dV, s);
+    case 64: return launch_bwd_small_t<__bf16, 64>(p, Q, K, V, dO, O, L, Dv, dQ, dK, dV, s);
+    case 80: return launch_bwd_small_t<__bf16, 80>(p, Q, K, V, dO, O, L, Dv, dQ, dK, dV, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 #define ATTN_BWD_CASES(X)                                     \
   X(__bf16, kBF16, 16) X(__bf16, kBF16, 32) X(__bf16, kBF16, 64) \
   X(__bf16, kBF16, 80) X(__bf16, kBF16, 128) X(float, kF32, 16) \
@@ -462,17 +588,21 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
 
 // Tile choices (measured on MI355X): for bf16 head dims up to 80, two 4-wave workgroups per CU with
 // 64-query stages (waves of different workgroups share a SIMD, so their MFMA and VALU phases
-// interleave); at d = 128 the register file only holds 2 waves per SIMD, so one 8-wave workgroup
-// with 32-query stages for large grids.
+// interleave).  At d = 128 the register file holds two waves per SIMD only with V in LDS: one
+// 8-wave workgroup per CU with 32-query stages for large grids, 4-wave workgroups otherwise.
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                        const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
-    if (DT == kF32) return launch_dkdv_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);        \
-    if (DD <= 80) return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s);          \
-    if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                               \
-      return launch_dkdv_t<T, DD, 8, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
-    return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                        \
+    if constexpr (DT == kF32) {                                                                     \
+      return launch_dkdv_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+    } else if constexpr (DD <= 80) {                                                                \
+      return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+    } else {                                                                                        \
+      if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                             \
+        return launch_dkdv_t<T, DD, 8, 32, 1, true>(p, Q, K, V, dO, L, Dv, dK, dV, s);              \
+      return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+    }                                                                                               \
   }
   ATTN_BWD_CASES(X)
 #undef X
@@ -484,9 +614,9 @@ hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, 
                      const void* O, const float* L, float* Dv, void* dQ, hipStream_t s) {
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
-    if (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s);           \
-    if (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);             \
-    return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);                           \
+    if constexpr (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s); \
+    else if constexpr (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s); \
+    else return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);                      \
   }
   ATTN_BWD_CASES(X)
 #undef X

@@ -228,11 +228,11 @@ __device__ __forceinline__ void settle(const F& f) { asm volatile("" ::"v"(f)); 
 // Block index -> logical work item, so that the 8 XCDs (which receive workgroups round-robin)
 // each get a contiguous range of logical items, i.e. whole heads, and share that head's K/V in
 // their own L2.  The grid is padded to a multiple of 8; padding blocks get -1.
-__device__ __forceinline__ int xcd_logical_block(int nlogical) {
+__device__ __forceinline__ int xcd_logical_block(int nlogical, int b) {
   const int per = (nlogical + 7) >> 3;
-  const int b = blockIdx.x;
   const int logical = (b & 7) * per + (b >> 3);
   return logical < nlogical ? logical : -1;
 }
+__device__ __forceinline__ int xcd_logical_block(int nlogical) { return xcd_logical_block(nlogical, blockIdx.x); }
 
 }  // namespace attn

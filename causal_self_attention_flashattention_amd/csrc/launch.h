@@ -35,4 +35,11 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
                      const void* dO, const void* O, const float* L, float* Dv, void* dQ, hipStream_t stream);
 
+// Small problems: the dQ and dK/dV work of attn_bwd in a single launch (both halves independent;
+// D stored by the dQ half).  bwd_small_applies tells when this path is used.
+bool bwd_small_applies(int dtype, const Problem& p);
+hipError_t launch_bwd_small(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
+                            const void* dO, const void* O, const float* L, float* Dv, void* dQ, void* dK,
+                            void* dV, hipStream_t stream);
+
 }  // namespace attn

@@ -96,6 +96,11 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, con
                 float* D, void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype,
                 const int32_t* kv_len, hipStream_t stream);
 
+/* How many kernels attn_bwd launches for this problem: 1 when the dQ and dK/dV work share one
+ * launch (small bfloat16 problems with d <= 80, where the grid would otherwise leave CUs idle),
+ * 2 otherwise (attn_bwd_dq with O, then attn_bwd_dkdv).  Negative attn_status on bad arguments. */
+int attn_bwd_launches(int B, int H, int N, int d, int dtype);
+
 /* Static text for a status code (never NULL). */
 const char* attn_status_string(int status);
 
