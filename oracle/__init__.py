@@ -9,6 +9,8 @@ from .attention import (  # noqa: F401
     attention_forward,
     head_backward,
     head_forward,
+    head_rows,
+    head_tail_keys,
     rowsum_o_do,
     rowsum_p_dp,
     valid_mask,

@@ -35,6 +35,8 @@ import numpy as np
 
 __all__ = [
     "valid_mask",
+    "head_rows",
+    "head_tail_keys",
     "head_forward",
     "head_backward",
     "attention_forward",
@@ -109,6 +111,77 @@ def head_backward(q, k, v, do, *, causal: bool, scale: float, kv: int | None = N
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv, d_ref
+
+
+def _row_terms(q, k, v, do, i, causal, scale, kv):
+    """Row i of the definition as vectors over its visible keys (no N x N matrix): returns the key
+    indices, p (eq. 5 row), L_i (eq. 12), and, when do is given, ds_i (eq. 9 row form) and D_i."""
+    n = k.shape[0]
+    hi = n if kv is None else kv
+    if causal:
+        hi = min(hi, i + 1)
+    if hi < 1:
+        raise ValueError("a query row has no unmasked key (kv_len must be >= 1)")
+    keys = np.arange(hi)
+    s = scale * (k[:hi] @ q[i])
+    m = s.max()
+    e = np.exp(s - m)
+    tot = e.sum()
+    p = e / tot
+    lse = m + np.log(tot)
+    if do is None:
+        return keys, p, lse, None, None
+    dp = v[:hi] @ do[i]  # dP_ij = do_i . v_j (eq. 8)
+    d_i = float(p @ dp)
+    ds = p * dp - p * d_i  # eq. 9, row form
+    return keys, p, lse, ds, d_i
+
+
+def head_rows(q, k, v, do, rows, *, causal: bool, scale: float, kv: int | None = None):
+    """Selected query rows of one head, each evaluated from its own row of the definition.
+
+    For row i: scores s_j = scale q_i . k_j over the visible keys, p = softmax(s) (eq. 5),
+    o_i = p V (eq. 6), L_i = log sum_j exp(s_j) (eq. 12); with do, the row form of eqs. (8)-(10):
+    dP_ij = do_i . v_j, D_i = p . dP_i, dS_i = p o dP_i - p D_i, dq_i = scale dS_i K.
+    Costs O(N d) per row, so it serves sequence lengths whose N x N matrices do not fit.
+    Returns ``(O [r, d], L [r], dQ [r, d] or None, D [r] or None)`` in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    do = None if do is None else _f64(do)
+    rows = [int(i) for i in rows]
+    o = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    dq = None if do is None else np.zeros((len(rows), q.shape[1]))
+    dd = None if do is None else np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        keys, p, l_i, ds, d_i = _row_terms(q, k, v, do, i, causal, scale, kv)
+        o[r] = p @ v[keys]
+        lse[r] = l_i
+        if do is not None:
+            dq[r] = scale * (ds @ k[keys])
+            dd[r] = d_i
+    return o, lse, dq, dd
+
+
+def head_tail_keys(q, k, v, do, ntail: int, *, scale: float):
+    """dK_j, dV_j (eqs. 7 and 11) for the last ``ntail`` keys of one causal head without padding.
+
+    Under the causal mask key j is seen only by queries i >= j, so for the last ntail keys the
+    sums over i run over the last ntail rows alone: dV_j = sum_i P_ij do_i, dK_j = scale sum_i
+    dS_ij q_i, with each row's P_i and dS_i from that row of the definition.
+    Returns ``(dK [ntail, d], dV [ntail, d])`` in float64, keys N - ntail .. N - 1.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n = k.shape[0]
+    j0 = n - ntail
+    dk = np.zeros((ntail, k.shape[1]))
+    dv = np.zeros((ntail, v.shape[1]))
+    for i in range(j0, n):
+        keys, p, _, ds, _ = _row_terms(q, k, v, do, i, True, scale, None)
+        sel = keys >= j0
+        dv[keys[sel] - j0] += p[sel, None] * do[i][None, :]
+        dk[keys[sel] - j0] += scale * ds[sel, None] * q[i][None, :]
+    return dk, dv
 
 
 def _kv_of(kv_len, b: int):

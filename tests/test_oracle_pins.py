@@ -353,3 +353,138 @@ def test_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"planted mistake {name!r} passed every pin"
+
+
+# --------------------------------------------------------------------------------------------
+# Row-wise oracle (head_rows, head_tail_keys): used at sequence lengths whose N x N matrices do not
+# fit.  Pinned against the full oracle above (itself pinned by closed forms, finite differences,
+# brute force and torch) and against closed forms; planted mistakes must fail a pin.
+
+
+def rpin_rows_match_full(impl):
+    """Every row from head_rows equals the same row of the materialised definition."""
+    r = _rng(21)
+    n, d = 45, 7
+    q, k, v, do = r.normal(size=(4, n, d))
+    for causal, kv in ((True, None), (False, None), (True, 30), (False, 12), (True, 1)):
+        o, lse, _ = O.head_forward(q, k, v, causal=causal, scale=0.45, kv=kv)
+        dq, _, _, dref = O.head_backward(q, k, v, do, causal=causal, scale=0.45, kv=kv)
+        rows = [0, 1, 13, 29, 30, 44]
+        ro, rl, rdq, rd = impl.head_rows(q, k, v, do, rows, causal=causal, scale=0.45, kv=kv)
+        np.testing.assert_allclose(ro, o[rows], atol=1e-13)
+        np.testing.assert_allclose(rl, lse[rows], atol=1e-13)
+        np.testing.assert_allclose(rdq, dq[rows], atol=1e-13)
+        np.testing.assert_allclose(rd, dref[rows], atol=1e-13)
+
+
+def rpin_rows_zero_query(impl):
+    """Q = 0: each row's output is the mean of its visible V rows, L_i = ln(#visible)."""
+    r = _rng(22)
+    n, d = 33, 4
+    k, v, do = r.normal(size=(3, n, d))
+    q = np.zeros((n, d))
+    for causal, kv in ((True, None), (True, 20), (False, 7)):
+        rows = list(range(n))
+        o, lse, _, _ = impl.head_rows(q, k, v, do, rows, causal=causal, scale=0.8, kv=kv)
+        for i in rows:
+            hi = n if kv is None else kv
+            if causal:
+                hi = min(hi, i + 1)
+            np.testing.assert_allclose(o[i], v[:hi].mean(0), atol=1e-13)
+            np.testing.assert_allclose(lse[i], math.log(hi), atol=1e-13)
+
+
+def rpin_tail_keys_match_full(impl):
+    """dK, dV of the last keys from their few query rows equal the materialised backward."""
+    r = _rng(23)
+    n, d = 38, 6
+    q, k, v, do = r.normal(size=(4, n, d))
+    _, dk, dv, _ = O.head_backward(q, k, v, do, causal=True, scale=0.55, kv=None)
+    for nt in (1, 5, 17):
+        tk, tv = impl.head_tail_keys(q, k, v, do, nt, scale=0.55)
+        np.testing.assert_allclose(tk, dk[n - nt:], atol=1e-13)
+        np.testing.assert_allclose(tv, dv[n - nt:], atol=1e-13)
+
+
+RPINS = [rpin_rows_match_full, rpin_rows_zero_query, rpin_tail_keys_match_full]
+
+
+@pytest.mark.parametrize("pin", RPINS, ids=lambda p: p.__name__)
+def test_row_oracle_pin(pin):
+    pin(O)
+
+
+def _rows_variant(kind):
+    def rows_fn(q, k, v, do, rows, *, causal, scale, kv=None):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        n = k.shape[0]
+        out = ([], [], [], [])
+        for i in rows:
+            hi = n if kv is None else kv
+            if causal:
+                hi = min(hi, i if kind == "causal_excludes_diagonal" and i > 0 else i + 1)
+            s = scale * (k[:hi] @ q[i])
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            dp = v[:hi] @ do[i]
+            d_i = p @ dp
+            ds = p * dp if kind == "drop_D" else p * dp - p * d_i
+            out[0].append(p @ v[:hi])
+            out[1].append(s.max() + np.log(e.sum()))
+            out[2].append((ds @ k[:hi]) if kind == "dq_no_scale" else scale * (ds @ k[:hi]))
+            out[3].append(d_i)
+        return tuple(np.array(x) for x in out)
+
+    return rows_fn
+
+
+def _tail_variant(kind):
+    def tail_fn(q, k, v, do, ntail, *, scale):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        n = k.shape[0]
+        j0 = n - ntail
+        dk = np.zeros((ntail, k.shape[1]))
+        dv = np.zeros((ntail, v.shape[1]))
+        first = j0 + 1 if kind == "skip_first_row" else j0
+        for i in range(first, n):
+            s = scale * (k[: i + 1] @ q[i])
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            dp = v[: i + 1] @ do[i]
+            ds = p * dp - p * (p @ dp)
+            for j in range(j0, i + 1):
+                dv[j - j0] += p[j] * do[i]
+                dk[j - j0] += (ds[j] * k[j]) * scale if kind == "dk_uses_k" else scale * ds[j] * q[i]
+        return dk, dv
+
+    return tail_fn
+
+
+ROW_MUTANTS = {
+    "rows_causal_excludes_diagonal": types.SimpleNamespace(head_rows=_rows_variant("causal_excludes_diagonal"),
+                                                           head_tail_keys=O.head_tail_keys),
+    "rows_drop_D": types.SimpleNamespace(head_rows=_rows_variant("drop_D"), head_tail_keys=O.head_tail_keys),
+    "rows_dq_no_scale": types.SimpleNamespace(head_rows=_rows_variant("dq_no_scale"), head_tail_keys=O.head_tail_keys),
+    "tail_skips_first_row": types.SimpleNamespace(head_rows=O.head_rows, head_tail_keys=_tail_variant("skip_first_row")),
+    "tail_dk_uses_k": types.SimpleNamespace(head_rows=O.head_rows, head_tail_keys=_tail_variant("dk_uses_k")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROW_MUTANTS))
+def test_planted_row_mistake_is_caught(name):
+    impl = ROW_MUTANTS[name]
+    failed = []
+    for pin in RPINS:
+        try:
+            pin(impl)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name!r} passed every row pin"
+
+
+def test_correct_variants_pass_row_pins():
+    """The mutant builders without a planted mistake pass every row pin (so failures above are
+    due to the planted mistake, not to the builders)."""
+    ok = types.SimpleNamespace(head_rows=_rows_variant("none"), head_tail_keys=_tail_variant("none"))
+    for pin in RPINS:
+        pin(ok)
