@@ -49,27 +49,28 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (head, 32*NW keys); loop over query tiles of BQ rows, double
-// buffered in LDS together with the tile's L*log2(e) and D values.
+// dK, dV: one workgroup per (head, 32*KB*NW keys); each wave owns KB blocks of 32 keys and loops
+// over query tiles of BQ rows, double buffered in LDS together with the tile's L*log2(e) and D
+// values.  With KB = 2 every Q / dO operand read from LDS feeds the products of two key blocks,
+// which halves the LDS read traffic per MFMA.
 
 // LDS bytes of the dK/dV body: two stages of (Q tile, dO tile, L row, D row), then either (DSELF)
 // one float of D per query row for rows up to kDselfMaxN, or (VLDS) the workgroup's V rows.
 constexpr int kDselfMaxN = 4096;
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS>
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int TILE = BQ * lds_pitch<T, DP>() * (int)sizeof(T);
   return 2 * (2 * TILE + 2 * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
-         (VLDS ? 32 * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0);
+         (VLDS ? 32 * KB * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0);
 }
 
 // One dK/dV work item (logical block `block` of the grid described by BH, N).  With DSELF the body
 // does not read D: it first computes D = rowsum(O o dO) for every query row it will visit, in the
 // same fragment order as the D pre-pass, into LDS (requires N <= kDselfMaxN).  With VLDS the
 // workgroup's V rows are kept in LDS and read per block instead of being held in registers (frees
-// 32 VGPRs per wave at d = 128, where the register file is otherwise too small for two waves per
-// SIMD without spilling).
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS>
+// 32 VGPRs per key block at d = 128, where the register file is otherwise too small).
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1>
 __device__ __forceinline__ void dkdv_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
@@ -77,7 +78,8 @@ __device__ __forceinline__ void dkdv_body(
     float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
-  constexpr int KT = 32 * NW;  // keys per workgroup
+  constexpr int KW = 32 * KB;  // keys per wave
+  constexpr int KT = KW * NW;  // keys per workgroup
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
@@ -103,15 +105,14 @@ __device__ __forceinline__ void dkdv_body(
 
   const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
   const int k0 = kt * KT;
-  const int kw = k0 + 32 * w;  // first key of this wave
-  const int key = kw + col;    // this lane's key
+  const int kw = k0 + KW * w;  // first key of this wave
   const bool wave_live = kw < kv;
-  // This lane's key is visible to queries q with qmin <= q < N (and never if key >= kv).
-  const int qmin = key >= kv ? N : (causal ? key : 0);
 
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 dk[KB][NDB], dv[KB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) { dk[kb][i] = f32x16{}; dv[kb][i] = f32x16{}; }
 
   if (k0 < kv) {
     const uint32_t tbytes = (uint32_t)(N * D * sizeof(T));
@@ -121,7 +122,7 @@ __device__ __forceinline__ void dkdv_body(
     const auto ro = make_rsrc(dO + base, tbytes);
     const auto rl = make_rsrc(Lse + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
     const auto rd = make_rsrc(Dv + (size_t)bh * N, (uint32_t)(N * sizeof(float)));
-    typename M::frag kf[KS], vf[VLDS ? 1 : KS];
+    typename M::frag kf[KB][KS], vf[KB][VLDS ? 1 : KS];
     lds_t* vt = lds + 2 * STAGE;  // VLDS: V rows k0 .. k0 + KT - 1
     if constexpr (VLDS) {
       TileCopy<T, KT, D, LD, NT> vcp;
@@ -129,15 +130,19 @@ __device__ __forceinline__ void dkdv_body(
       vcp.store(vt);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = frag_global<T>(rk, key, D, ks * M::KSTEP);
-      if constexpr (!VLDS) vf[ks] = frag_global<T>(rv, key, D, ks * M::KSTEP);
-    }
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      settle(kf[ks]);
-      if constexpr (!VLDS) settle(vf[ks]);
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[kb][ks] = frag_global<T>(rk, kw + 32 * kb + col, D, ks * M::KSTEP);
+        if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
+      }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        settle(kf[kb][ks]);
+        if constexpr (!VLDS) settle(vf[kb][ks]);
+      }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
     const int nqt = TQ - qt0;
@@ -205,24 +210,37 @@ __device__ __forceinline__ void dkdv_body(
         for (int qb = 0; qb < NQB; ++qb) {
           const int qb0 = q0 + qb * 32;
           if (qb0 >= N || (causal && qb0 + 31 < kw)) continue;  // past the end, or before this wave's keys
-          f32x16 s = f32x16{}, dp = f32x16{};
+          f32x16 s[KB], dp[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            s = M::mma(M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP), kf[ks], s);
-            if constexpr (VLDS)
-              dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP),
-                          M::frag_direct(vt, LD, w * 32 * LD + ks * M::KSTEP), dp);
-            else
-              dp = M::mma(M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP), vf[ks], dp);
+            const typename M::frag qa = M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP);
+            const typename M::frag oa = M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              s[kb] = M::mma(qa, kf[kb][ks], s[kb]);
+              if constexpr (VLDS)
+                dp[kb] = M::mma(oa, M::frag_direct(vt, LD, (w * KW + 32 * kb) * LD + ks * M::KSTEP), dp[kb]);
+              else
+                dp[kb] = M::mma(oa, vf[kb][ks], dp[kb]);
+            }
           }
           // Mask only blocks that cross the diagonal, the key end or the sequence end: a score
-          // whose query row is outside [qmin, N) is pushed to kMaskedScore so exp2 gives 0.
-          if ((causal && kw + 31 > qb0) || (kw + 32 > kv) || (qb0 + 32 > N)) {
-            const int lo = qmin - qb0, hi = N - qb0;
+          // whose query row is outside [qmin, N) is pushed to kMaskedScore so exp2 gives 0.  A key
+          // block lying wholly above the diagonal comes out all masked (weights exactly 0).
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int r = acc_row(e, half);
-              s[e] = (r < lo || r >= hi) ? kMaskedScore : s[e];
+          for (int kb = 0; kb < KB; ++kb) {
+            const int kbw = kw + 32 * kb;
+            if ((causal && kbw + 31 > qb0) || (kbw + 32 > kv) || (qb0 + 32 > N)) {
+              const int key = kbw + col;
+              const int qmin = key >= kv ? N : (causal ? key : 0);
+              const int lo = qmin - qb0, hi = N - qb0;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int r = acc_row(e, half);
+                s[kb][e] = (r < lo || r >= hi) ? kMaskedScore : s[kb][e];
+              }
             }
           }
 #pragma unroll
@@ -231,21 +249,32 @@ __device__ __forceinline__ void dkdv_body(
             const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lrow + r0);
             const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + r0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 4 * m + r;
-              const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lv[r]));
-              s[e] = p;
-              dp[e] = p * (dp[e] - dd[r]);
-            }
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int e = 4 * m + r;
+                const float p = fast_exp2(__builtin_fmaf(s[kb][e], scale_log2, -lv[r]));
+                s[kb][e] = p;
+                dp[kb][e] = p * (dp[kb][e] - dd[r]);
+              }
           }
 #pragma unroll
           for (int c = 0; c < M::CALLS32; ++c) {
-            const typename M::frag pf = M::acc_frag(s, c);
-            const typename M::frag sf = M::acc_frag(dp, c);
+            typename M::frag pf[KB], sf[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              pf[kb] = M::acc_frag(s[kb], c);
+              sf[kb] = M::acc_frag(dp[kb], c);
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              dv[db] = M::mma(M::frag_trans(otile, LD, qb * 32 * LD + db * 32, c), pf, dv[db]);
-              dk[db] = M::mma(M::frag_trans(qtile, LD, qb * 32 * LD + db * 32, c), sf, dk[db]);
+              const typename M::frag ot = M::frag_trans(otile, LD, qb * 32 * LD + db * 32, c);
+              const typename M::frag qt = M::frag_trans(qtile, LD, qb * 32 * LD + db * 32, c);
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb) {
+                dv[kb][db] = M::mma(ot, pf[kb], dv[kb][db]);
+                dk[kb][db] = M::mma(qt, sf[kb], dk[kb][db]);
+              }
             }
           }
         }
@@ -256,47 +285,51 @@ __device__ __forceinline__ void dkdv_body(
     }
   }
 
-  if (key < N) {
-    T* krow = dK + (size_t)key * D;
-    T* vrow = dV + (size_t)key * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw + 32 * kb + col;
+    if (key < N) {
+      T* krow = dK + (size_t)key * D;
+      T* vrow = dV + (size_t)key * D;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int d0 = db * 32 + 8 * m + 4 * half;
-        if (D % 32 == 0 || d0 < D) {
-          T kk[4], vv[4];
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            kk[r] = (T)(dk[db][4 * m + r] * scale);
-            vv[r] = (T)dv[db][4 * m + r];
-          }
-          if constexpr (sizeof(T) == 2) {
-            uint2 u;
-            __builtin_memcpy(&u, kk, 8);
-            *reinterpret_cast<uint2*>(krow + d0) = u;
-            __builtin_memcpy(&u, vv, 8);
-            *reinterpret_cast<uint2*>(vrow + d0) = u;
-          } else {
-            uint4 u;
-            __builtin_memcpy(&u, kk, 16);
-            *reinterpret_cast<uint4*>(krow + d0) = u;
-            __builtin_memcpy(&u, vv, 16);
-            *reinterpret_cast<uint4*>(vrow + d0) = u;
+        for (int m = 0; m < 4; ++m) {
+          const int d0 = db * 32 + 8 * m + 4 * half;
+          if (D % 32 == 0 || d0 < D) {
+            T kk[4], vv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              kk[r] = (T)(dk[kb][db][4 * m + r] * scale);
+              vv[r] = (T)dv[kb][db][4 * m + r];
+            }
+            if constexpr (sizeof(T) == 2) {
+              uint2 u;
+              __builtin_memcpy(&u, kk, 8);
+              *reinterpret_cast<uint2*>(krow + d0) = u;
+              __builtin_memcpy(&u, vv, 8);
+              *reinterpret_cast<uint2*>(vrow + d0) = u;
+            } else {
+              uint4 u;
+              __builtin_memcpy(&u, kk, 16);
+              *reinterpret_cast<uint4*>(krow + d0) = u;
+              __builtin_memcpy(&u, vv, 16);
+              *reinterpret_cast<uint4*>(vrow + d0) = u;
+            }
           }
         }
-      }
+    }
   }
 }
 
-template <typename T, int D, int NW, int BQ, int OCC, bool VLDS>
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB = 1>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
     int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
-  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS>()];
-  dkdv_body<T, D, NW, BQ, false, VLDS>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N, causal,
-                                       scale, scale_log2, kv_len);
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB>()];
+  dkdv_body<T, D, NW, BQ, false, VLDS, KB>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N,
+                                           causal, scale, scale_log2, kv_len);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -514,14 +547,14 @@ static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* d
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int BQ, int OCC, bool VLDS = false>
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS = false, int KB = 1>
 static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
-  constexpr int KT = 32 * NW;
+  constexpr int KT = 32 * KB * NW;
   const int TK = (p.N + KT - 1) / KT;
   const int nlog = p.B * p.H * TK;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
+  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
                      (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal, p.scale,
                      p.scale * kLog2e, p.kv_len);
   return hipGetLastError();

@@ -79,8 +79,8 @@ int attn_bwd_rowdot(const void* O, const void* dO, float* D, int B, int H, int N
                     hipStream_t stream);
 
 /* The backward's second step alone: dK and dV for every key tile (eqs. 13-17 and 19 of the
- * handout, §4.1), P recomputed from L, D taken from attn_bwd_rowdot.  Arguments as for attn_bwd;
- * D is an input here.  attn_bwd = attn_bwd_rowdot, then attn_bwd_dkdv, then attn_bwd_dq. */
+ * handout, §4.1), P recomputed from L, D taken from attn_bwd_rowdot (or from attn_bwd_dq called
+ * with O).  Arguments as for attn_bwd; D is an input here. */
 int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
                   void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, int dtype,
                   const int32_t* kv_len, hipStream_t stream);
