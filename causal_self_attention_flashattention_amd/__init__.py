@@ -16,5 +16,6 @@ from .binding import (  # noqa: F401
     status_string,
     supported,
 )
+from .function import FlashAttention, flash_attention  # noqa: F401
 
-__all__ = ["fwd", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]
+__all__ = ["FlashAttention", "flash_attention", "fwd", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

@@ -95,7 +95,8 @@ def _check_qkv(*ts):
     return ref.shape
 
 
-def _kv_tensor(kv_len, B, device):
+def kv_len_tensor(kv_len, B, device):
+    """kv_len (None, an int, a sequence of B ints or an int tensor) as a device int32[B] tensor or None."""
     if kv_len is None:
         return None
     if isinstance(kv_len, torch.Tensor):
@@ -114,7 +115,7 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, o
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    kv = _kv_tensor(kv_len, B, q.device)
+    kv = kv_len_tensor(kv_len, B, q.device)
     st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)),
                                  scale, _DTYPES[q.dtype], _ptr(kv), _stream())
     _check("attn_fwd", st)
@@ -130,7 +131,7 @@ def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv
         D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         dq, dk, dv, D = outs
-    kv = _kv_tensor(kv_len, B, q.device)
+    kv = kv_len_tensor(kv_len, B, q.device)
     st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
                                  _ptr(kv), _stream())
@@ -152,7 +153,7 @@ def bwd_dkdv(q, k, v, do, lse, D, causal: bool = True, scale: float | None = Non
     B, H, N, d = _check_qkv(q, k, v, do)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dk, dv = (torch.empty_like(k), torch.empty_like(v)) if outs is None else outs
-    kv = _kv_tensor(kv_len, B, q.device)
+    kv = kv_len_tensor(kv_len, B, q.device)
     st = load_library().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _ptr(dk), _ptr(dv),
                                       B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
     _check("attn_bwd_dkdv", st)
@@ -167,7 +168,7 @@ def bwd_dq(q, k, v, do, lse, D, causal: bool = True, scale: float | None = None,
         _check_qkv(q, o)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if out is None else out
-    kv = _kv_tensor(kv_len, B, q.device)
+    kv = kv_len_tensor(kv_len, B, q.device)
     st = load_library().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o), _ptr(lse), _ptr(D), _ptr(dq), B, H,
                                     N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
     _check("attn_bwd_dq", st)
