@@ -21,6 +21,14 @@ What it computes, and where that is defined:
   It deliberately does not use the ``D = rowsum(O o dO)`` shortcut of eqs. (13)-(19); the
   row dot product ``P_i . dP_i`` is taken from P and dP, so the oracle is independent of the
   pre-pass it is used to check.  ``rowsum_p_dp`` returns that dot product as ``D_ref``.
+* Block-sparse masking: the "Block-sparse Flashattention" section of "Notes on flashattention"
+  restricts the scores to the support of a mask M that is constant on blocks: entry (i, j) is
+  kept iff ``block_mask[i // block, j // block]`` is non-zero.  The page writes the masked score
+  as 0; read literally that would give masked keys weight exp(0), which contradicts the same
+  section's point that zero blocks need no work at all, so here (as for the causal mask) a
+  masked entry has weight exactly 0.  A row left with no key at all has no softmax; for it the
+  oracle returns O = 0, L = -inf and zero gradients (a block mask can produce such rows; causal
+  and key-padding masks with kv >= 1 cannot).
 * Theorem 1 of "Notes on flashattention" (section Analysis / Correctness) shows the tiled
   online-softmax forward returns exactly ``softmax(S) V``; that is why an untiled, materialised
   reference is the right thing to compare a tiled kernel against.
@@ -55,12 +63,14 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def valid_mask(n: int, causal: bool, kv: int | None) -> np.ndarray:
+def valid_mask(n: int, causal: bool, kv: int | None, block_mask=None, block: int = 64) -> np.ndarray:
     """Boolean ``[n, n]`` matrix, True where query i may attend key j.
 
     Causal (handout Problem (flash_forward)(c)): key j is masked for query i when j > i; the
     diagonal is kept (square mask, equal query and key lengths).  Key padding: keys j >= kv are
-    masked for every query.  ``kv=None`` means no padding.
+    masked for every query.  ``kv=None`` means no padding.  Block-sparse ("Notes on
+    flashattention", Block-sparse Flashattention): ``block_mask`` is a ``[ceil(n/block)]^2``
+    array and (i, j) is kept only where ``block_mask[i // block, j // block]`` is non-zero.
     """
     i = np.arange(n)[:, None]
     j = np.arange(n)[None, :]
@@ -69,33 +79,43 @@ def valid_mask(n: int, causal: bool, kv: int | None) -> np.ndarray:
         ok &= j <= i
     if kv is not None:
         ok &= j < kv
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        tb = -(-n // block)
+        if bm.shape != (tb, tb):
+            raise ValueError(f"block_mask must be [{tb}, {tb}] for n={n}, block={block}")
+        ok &= bm[i // block, j // block]
     return ok
 
 
-def head_forward(q, k, v, *, causal: bool, scale: float, kv: int | None = None):
+def head_forward(q, k, v, *, causal: bool, scale: float, kv: int | None = None, block_mask=None,
+                 block: int = 64):
     """One head. q, k, v: ``[N, d]``. Returns ``(O [N, d], L [N], P [N, N])`` in float64.
 
     Eq. (4): S = scale * q k^T.  Eq. (5): row softmax over the unmasked entries (shifted by the
     row maximum for stability; the shift cancels).  Eq. (6): O = P v.  Eq. (12): L = log of the
     row sum of exp(S) over unmasked entries, written as m + log(sum exp(S - m)).
-    Every row must keep at least one key (kv >= 1); a fully masked row is rejected.
+    Without a block mask every row must keep at least one key (kv >= 1) and a fully masked row is
+    rejected; with one, a row left without keys gets P = 0, O = 0 and L = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n = q.shape[0]
-    ok = valid_mask(n, causal, kv)
-    if not ok.any(axis=1).all():
+    ok = valid_mask(n, causal, kv, block_mask, block)
+    live = ok.any(axis=1)
+    if block_mask is None and not live.all():
         raise ValueError("a query row has no unmasked key (kv_len must be >= 1)")
     s = scale * (q @ k.T)
-    m = np.where(ok, s, -np.inf).max(axis=1)
+    m = np.where(live, np.where(ok, s, -np.inf).max(axis=1), 0.0)
     e = np.where(ok, np.exp(np.where(ok, s, 0.0) - m[:, None]), 0.0)
     denom = e.sum(axis=1)
-    p = e / denom[:, None]
-    lse = m + np.log(denom)
+    p = e / np.where(live, denom, 1.0)[:, None]
+    lse = np.where(live, m + np.log(np.where(live, denom, 1.0)), -np.inf)
     o = p @ v
     return o, lse, p
 
 
-def head_backward(q, k, v, do, *, causal: bool, scale: float, kv: int | None = None):
+def head_backward(q, k, v, do, *, causal: bool, scale: float, kv: int | None = None, block_mask=None,
+                  block: int = 64):
     """One head. Returns ``(dQ, dK, dV, D_ref)`` in float64 via the textbook eqs. (7)-(11).
 
     dV = P^T dO (7); dP = dO v^T (8); dS_i = P_i o dP_i - P_i (P_i . dP_i) which is eq. (9)'s
@@ -103,7 +123,7 @@ def head_backward(q, k, v, do, *, causal: bool, scale: float, kv: int | None = N
     D_ref is the row dot product P_i . dP_i taken on the way.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    _, _, p = head_forward(q, k, v, causal=causal, scale=scale, kv=kv)
+    _, _, p = head_forward(q, k, v, causal=causal, scale=scale, kv=kv, block_mask=block_mask, block=block)
     dv = p.T @ do
     dp = do @ v.T
     d_ref = (p * dp).sum(axis=1)
@@ -190,11 +210,13 @@ def _kv_of(kv_len, b: int):
     return int(np.asarray(kv_len).reshape(-1)[b])
 
 
-def attention_forward(q, k, v, *, causal: bool, scale: float, kv_len=None, heads=None):
+def attention_forward(q, k, v, *, causal: bool, scale: float, kv_len=None, heads=None, block_mask=None,
+                      block: int = 64):
     """Batched forward over ``[B, H, N, d]``. Returns ``(O [B,H,N,d], L [B,H,N])`` float64.
 
     ``kv_len``: per-batch key lengths ``[B]`` or None. ``heads``: optional list of ``(b, h)``
     pairs; when given only those heads are computed and the result arrays hold NaN elsewhere.
+    ``block_mask``: optional ``[ceil(N/block)]^2`` block-sparse mask shared by every head.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
@@ -202,12 +224,14 @@ def attention_forward(q, k, v, *, causal: bool, scale: float, kv_len=None, heads
     lse = np.full((B, H, N), np.nan)
     for b, h in heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]:
         o[b, h], lse[b, h], _ = head_forward(
-            q[b, h], k[b, h], v[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b)
+            q[b, h], k[b, h], v[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b), block_mask=block_mask,
+            block=block
         )
     return o, lse
 
 
-def attention_backward(q, k, v, do, *, causal: bool, scale: float, kv_len=None, heads=None):
+def attention_backward(q, k, v, do, *, causal: bool, scale: float, kv_len=None, heads=None, block_mask=None,
+                       block: int = 64):
     """Batched backward. Returns ``(dQ, dK, dV, D_ref)`` float64 (NaN outside ``heads`` if given)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
@@ -217,7 +241,8 @@ def attention_backward(q, k, v, do, *, causal: bool, scale: float, kv_len=None, 
     dref = np.full((B, H, N), np.nan)
     for b, h in heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]:
         dq[b, h], dk[b, h], dv[b, h], dref[b, h] = head_backward(
-            q[b, h], k[b, h], v[b, h], do[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b)
+            q[b, h], k[b, h], v[b, h], do[b, h], causal=causal, scale=scale, kv=_kv_of(kv_len, b),
+            block_mask=block_mask, block=block
         )
     return dq, dk, dv, dref
 
