@@ -27,6 +27,9 @@ SIGNATURES = {
     "attn_bwd_rowdot": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "attn_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "attn_fwd_blocksparse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]),
+    "attn_bwd_blocksparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                  _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
     "attn_bwd_launches": (_i, [_i, _i, _i, _i, _i]),
@@ -109,21 +112,50 @@ def kv_len_tensor(kv_len, B, device):
     return t
 
 
-def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, out=None, lse=None):
-    """Attention forward. Returns ``(O, L)``: O like q, L float32 [B, H, N] (natural log)."""
+def mask_blocks(N: int) -> int:
+    """Side of a block-sparse mask for sequence length N (one entry per 64 x 64 block)."""
+    return (N + 63) // 64
+
+
+def block_mask_tensor(block_mask, N, device):
+    """block_mask (array-like or tensor, [ceil(N/64)]^2, non-zero = attend) as a device uint8 tensor."""
+    if block_mask is None:
+        return None
+    tb = mask_blocks(N)
+    m = block_mask if isinstance(block_mask, torch.Tensor) else torch.as_tensor(block_mask)
+    if tuple(m.shape) != (tb, tb):
+        raise ValueError(f"block_mask must be [{tb}, {tb}] for N={N} (one entry per 64 x 64 block)")
+    return (m != 0).to(device=device, dtype=torch.uint8).contiguous()
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, out=None, lse=None,
+        block_mask=None):
+    """Attention forward. Returns ``(O, L)``: O like q, L float32 [B, H, N] (natural log).
+
+    ``block_mask`` (optional, [ceil(N/64)]^2, non-zero = attend) restricts the scores to whole
+    64 x 64 blocks (block-sparse attention); masked blocks are skipped by the kernels."""
     B, H, N, d = _check_qkv(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     kv = kv_len_tensor(kv_len, B, q.device)
-    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)),
-                                 scale, _DTYPES[q.dtype], _ptr(kv), _stream())
-    _check("attn_fwd", st)
+    bm = block_mask_tensor(block_mask, N, q.device)
+    lib = load_library()
+    if bm is None:
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)), scale,
+                          _DTYPES[q.dtype], _ptr(kv), _stream())
+        _check("attn_fwd", st)
+    else:
+        st = lib.attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)),
+                                      scale, _DTYPES[q.dtype], _ptr(kv), _ptr(bm), _stream())
+        _check("attn_fwd_blocksparse", st)
     return o, L
 
 
-def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv_len=None, outs=None):
-    """Attention backward. Returns ``(dQ, dK, dV, D)``; D = rowsum(O o dO) float32 [B, H, N]."""
+def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv_len=None, outs=None,
+        block_mask=None):
+    """Attention backward. Returns ``(dQ, dK, dV, D)``; D = rowsum(O o dO) float32 [B, H, N].
+    ``block_mask`` as for :func:`fwd` (the same mask the forward used)."""
     B, H, N, d = _check_qkv(q, k, v, o, do)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if outs is None:
@@ -132,10 +164,17 @@ def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv
     else:
         dq, dk, dv, D = outs
     kv = kv_len_tensor(kv_len, B, q.device)
-    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
-                                 _ptr(kv), _stream())
-    _check("attn_bwd", st)
+    bm = block_mask_tensor(block_mask, N, q.device)
+    lib = load_library()
+    if bm is None:
+        st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
+        _check("attn_bwd", st)
+    else:
+        st = lib.attn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
+                                      _ptr(kv), _ptr(bm), _stream())
+        _check("attn_bwd_blocksparse", st)
     return dq, dk, dv, D
 
 

@@ -24,6 +24,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_size(int dtype) { return dtype == ATTN_DTYPE_BF16 ? 2 : 4; }
 
+// Block-sparse masks hold one byte per 64 x 64 block; the kernels keep one row of it in LDS.
+constexpr int kMaxBlockSparseN = 65536;
+int mask_blocks(int N) { return (N + 63) / 64; }
+
 int check_common(int B, int H, int N, int d, int dtype, float scale, bool need_scale) {
   if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_E_DTYPE;
   if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_E_SHAPE;
@@ -137,6 +141,60 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   }
   // The dQ kernel computes D for its query rows on the way (replacing the separate pre-pass), so it
   // runs first; the dK/dV kernel then reads D.
+  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  return ATTN_OK;
+}
+
+int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
+                         int d, int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
+                         hipStream_t stream) {
+  if (!block_mask) return attn_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, kv_len, stream);
+  if (!Q || !K || !V || !O || !L) return ATTN_E_NULL;
+  int st = check_common(B, H, N, d, dtype, scale, true);
+  if (st != ATTN_OK) return st;
+  if (N > kMaxBlockSparseN) return ATTN_E_SHAPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(L)) return ATTN_E_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const size_t mb = (size_t)mask_blocks(N) * mask_blocks(N);
+  const Range outs[2] = {range_of(O, tb), range_of(L, lb)};
+  const Range ins[5] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb),
+                        kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}, range_of(block_mask, mb)};
+  st = check_alias(outs, 2, ins, 5);
+  if (st != ATTN_OK) return st;
+  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
+  if (attn::launch_fwd(dtype, p, Q, K, V, O, L, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  return ATTN_OK;
+}
+
+int attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                         void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                         int dtype, const int32_t* kv_len, const uint8_t* block_mask, hipStream_t stream) {
+  if (!block_mask)
+    return attn_bwd(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, causal, scale, dtype, kv_len, stream);
+  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !D) return ATTN_E_NULL;
+  int st = check_common(B, H, N, d, dtype, scale, true);
+  if (st != ATTN_OK) return st;
+  if (N > kMaxBlockSparseN) return ATTN_E_SHAPE;
+  const void* ptrs[] = {Q, K, V, O, dO, L, dQ, dK, dV, D};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_E_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const size_t mb = (size_t)mask_blocks(N) * mask_blocks(N);
+  const Range outs[4] = {range_of(dQ, tb), range_of(dK, tb), range_of(dV, tb), range_of(D, lb)};
+  const Range ins[8] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(O, tb), range_of(dO, tb),
+                        range_of(L, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0},
+                        range_of(block_mask, mb)};
+  st = check_alias(outs, 4, ins, 8);
+  if (st != ATTN_OK) return st;
+  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
+  if (attn::bwd_small_applies(dtype, p)) {
+    if (attn::launch_bwd_small(dtype, p, Q, K, V, dO, O, L, D, dQ, dK, dV, stream) != hipSuccess)
+      return ATTN_E_LAUNCH;
+    return ATTN_OK;
+  }
   if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
   if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream) != hipSuccess) return ATTN_E_LAUNCH;
   return ATTN_OK;

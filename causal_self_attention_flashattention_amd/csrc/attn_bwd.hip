@@ -57,25 +57,27 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 // LDS bytes of the dK/dV body: two stages of (Q tile, dO tile, L row, D row), then either (DSELF)
 // one float of D per query row for rows up to kDselfMaxN, or (VLDS) the workgroup's V rows.
 constexpr int kDselfMaxN = 4096;
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1>
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int TILE = BQ * lds_pitch<T, DP>() * (int)sizeof(T);
   return 2 * (2 * TILE + 2 * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
-         (VLDS ? 32 * KB * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0);
+         (VLDS ? 32 * KB * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0) + (BSP ? kMaxMaskBlocks : 0);
 }
 
 // One dK/dV work item (logical block `block` of the grid described by BH, N).  With DSELF the body
 // does not read D: it first computes D = rowsum(O o dO) for every query row it will visit, in the
 // same fragment order as the D pre-pass, into LDS (requires N <= kDselfMaxN).  With VLDS the
 // workgroup's V rows are kept in LDS and read per block instead of being held in registers (frees
-// 32 VGPRs per key block at d = 128, where the register file is otherwise too small).
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1>
+// 32 VGPRs per key block at d = 128, where the register file is otherwise too small).  With BSP
+// the query tiles whose mask row meets none of the workgroup's key blocks are skipped, and each
+// wave skips the tiles its own mask block excludes.
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false>
 __device__ __forceinline__ void dkdv_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
     const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal,
-    float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
+    float scale, float scale_log2, const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int KW = 32 * KB;  // keys per wave
@@ -87,9 +89,13 @@ __device__ __forceinline__ void dkdv_body(
   constexpr int LD = lds_pitch<T, DP>();
   constexpr int TILE = BQ * LD * (int)sizeof(T);
   constexpr int STAGE = 2 * TILE + 2 * BQ * (int)sizeof(float);  // Q tile, dO tile, L row, D row
+  constexpr int SHIFT = BQ == 64 ? 0 : 1;                        // query tiles per mask block = 1 << SHIFT
   static_assert(2 * BQ <= NT, "one thread per staged L / D value");
+  static_assert(!BSP || ((BQ == 32 || BQ == 64) && KT % kMaskBlock == 0 && KT / kMaskBlock <= 8),
+                "block-sparse tiles must nest in the 64 x 64 mask blocks");
 
   lds_t* lds = (lds_t*)smem;
+  lds_t* map = lds + dkdv_lds_bytes<T, D, NW, BQ, DSELF, VLDS, KB, false>();
 
   const int TK = (N + KT - 1) / KT;
   const int logical = xcd_logical_block(BH * TK, block);
@@ -107,6 +113,7 @@ __device__ __forceinline__ void dkdv_body(
   const int k0 = kt * KT;
   const int kw = k0 + KW * w;  // first key of this wave
   const bool wave_live = kw < kv;
+  const unsigned wave_bit = 1u << ((KW * w) / kMaskBlock);  // this wave's mask column within the workgroup
 
   f32x16 dk[KB][NDB], dv[KB][NDB];
 #pragma unroll
@@ -145,7 +152,6 @@ __device__ __forceinline__ void dkdv_body(
       }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
-    const int nqt = TQ - qt0;
 
     // DSELF: D for rows [qt0*BQ, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
@@ -193,19 +199,33 @@ __device__ __forceinline__ void dkdv_body(
         reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
             threadIdx.x < BQ ? lrd * kLog2e : lrd;
     };
-    load_stage(qt0);
-    store_stage(lds);
+    // Query tiles in loop order: all of [qt0, TQ), or (block-sparse) those whose mask row meets one
+    // of this workgroup's key blocks; current, next and next-but-one are tracked for the pipeline.
+    int cur = qt0;
+    if constexpr (BSP) {
+      build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, k0 / kMaskBlock, KT / kMaskBlock, true, NT);
+      __syncthreads();
+      cur = next_live_tile(map, qt0, TQ, SHIFT);
+    }
+    auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, TQ, SHIFT) : t + 1; };
+    if (cur < TQ) {
+      load_stage(cur);
+      store_stage(lds);
+    }
     __syncthreads();
-    if (nqt > 1) load_stage(qt0 + 1);
+    int nxt = cur < TQ ? after(cur) : TQ;
+    if (nxt < TQ) load_stage(nxt);
 
-    for (int it = 0; it < nqt; ++it) {
-      const int q0 = (qt0 + it) * BQ;
+    for (int it = 0; cur < TQ; ++it) {
+      const int q0 = cur * BQ;
       const lds_t* qtile = lds + (it & 1) * STAGE;
       const lds_t* otile = qtile + TILE;
       const __attribute__((address_space(3))) float* lrow =
           reinterpret_cast<const __attribute__((address_space(3))) float*>(qtile + 2 * TILE);
-      const __attribute__((address_space(3))) float* drow = DSELF ? dself + it * BQ : lrow + BQ;
-      if (wave_live) {
+      const __attribute__((address_space(3))) float* drow = DSELF ? dself + (cur - qt0) * BQ : lrow + BQ;
+      bool run = wave_live;
+      if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
+      if (run) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           const int qb0 = q0 + qb * 32;
@@ -279,9 +299,12 @@ __device__ __forceinline__ void dkdv_body(
           }
         }
       }
-      if (it + 1 < nqt) store_stage(lds + ((it + 1) & 1) * STAGE);
+      const int nxt2 = nxt < TQ ? after(nxt) : TQ;
+      if (nxt < TQ) store_stage(lds + ((it + 1) & 1) * STAGE);
       __syncthreads();
-      if (it + 2 < nqt) load_stage(qt0 + it + 2);
+      if (nxt2 < TQ) load_stage(nxt2);
+      cur = nxt;
+      nxt = nxt2;
     }
   }
 
@@ -322,31 +345,32 @@ __device__ __forceinline__ void dkdv_body(
   }
 }
 
-template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB = 1>
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB, bool BSP>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
-    int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
-  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB>()];
-  dkdv_body<T, D, NW, BQ, false, VLDS, KB>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N,
-                                           causal, scale, scale_log2, kv_len);
+    int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
+    const uint8_t* __restrict__ bmask) {
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB, BSP>()];
+  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N,
+                                                causal, scale, scale_log2, kv_len, bmask);
 }
 
 // ------------------------------------------------------------------------------------------
 // dQ: one workgroup per (head, 32*NW queries); loop over key tiles of BK rows, double buffered.
 
-template <typename T, int D, int BK>
+template <typename T, int D, int BK, bool BSP = false>
 constexpr int dq_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
-  return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T);
+  return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T) + (BSP ? kMaxMaskBlocks : 0);
 }
 
-template <typename T, int D, int NW, int BK>
+template <typename T, int D, int NW, int BK, bool BSP = false>
 __device__ __forceinline__ void dq_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
     T* __restrict__ dQ, int BH, int H, int N, int causal, float scale, float scale_log2,
-    const int32_t* __restrict__ kv_len) {
+    const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask) {
   // With Oin != nullptr the kernel first computes D = rowsum(O o dO) for its own query rows (each
   // row belongs to exactly one workgroup) and stores it to Dv for the dK/dV kernel that follows;
   // otherwise it reads D from Dv.
@@ -359,8 +383,12 @@ __device__ __forceinline__ void dq_body(
   constexpr int NB = BK / 32;
   constexpr int LD = lds_pitch<T, DP>();
   constexpr int TILE = BK * LD * (int)sizeof(T);
+  constexpr int SHIFT = BK == 64 ? 0 : 1;  // key tiles per mask block = 1 << SHIFT
+  static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
+                "block-sparse tiles must nest in the 64 x 64 mask blocks");
 
   lds_t* lds = (lds_t*)smem;
+  lds_t* map = lds + 4 * TILE;
 
   const int TQ = (N + QT - 1) / QT;
   const int logical = xcd_logical_block(BH * TQ, block);
@@ -381,6 +409,7 @@ __device__ __forceinline__ void dq_body(
   const int qw_last = min(qw + 31, N - 1);
   const bool wave_live = qw < N;
   const int lim = causal ? min(q, kv - 1) : kv - 1;
+  const unsigned wave_bit = 1u << ((32 * w) / kMaskBlock);  // this wave's mask row within the workgroup
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
@@ -426,23 +455,36 @@ __device__ __forceinline__ void dq_body(
     zero_pad_cols<T, BK, D, LD, DP, NT>(lds);
     zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 2 * TILE);
   }
-  TileCopy<T, BK, D, LD, NT> kc, vc;
-  kc.load(rk, 0);
-  vc.load(rv, 0);
-  kc.store(lds);
-  vc.store(lds + TILE);
-  __syncthreads();
-  if (nkt > 1) {
-    kc.load(rk, BK);
-    vc.load(rv, BK);
+  // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
+  int cur = 0;
+  if constexpr (BSP) {
+    build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
+    __syncthreads();
+    cur = next_live_tile(map, 0, nkt, SHIFT);
   }
-  for (int kt = 0; kt < nkt; ++kt) {
-    const lds_t* ktile = lds + (kt & 1) * 2 * TILE;
+  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, nkt, SHIFT) : t + 1; };
+  TileCopy<T, BK, D, LD, NT> kc, vc;
+  if (cur < nkt) {
+    kc.load(rk, cur * BK);
+    vc.load(rv, cur * BK);
+    kc.store(lds);
+    vc.store(lds + TILE);
+  }
+  __syncthreads();
+  int nxt = cur < nkt ? after(cur) : nkt;
+  if (nxt < nkt) {
+    kc.load(rk, nxt * BK);
+    vc.load(rv, nxt * BK);
+  }
+  for (int it = 0; cur < nkt; ++it) {
+    const lds_t* ktile = lds + (it & 1) * 2 * TILE;
     const lds_t* vtile = ktile + TILE;
-    if (wave_live) {
+    bool run = wave_live;
+    if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
+    if (run) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int kb0 = kt * BK + nb * 32;
+        const int kb0 = cur * BK + nb * 32;
         if (kb0 >= kend || (causal && kb0 > qw_last)) continue;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -468,16 +510,19 @@ __device__ __forceinline__ void dq_body(
         }
       }
     }
-    if (kt + 1 < nkt) {
-      lds_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
-      kc.store(nxt);
-      vc.store(nxt + TILE);
+    const int nxt2 = nxt < nkt ? after(nxt) : nkt;
+    if (nxt < nkt) {
+      lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
+      kc.store(st);
+      vc.store(st + TILE);
     }
     __syncthreads();
-    if (kt + 2 < nkt) {
-      kc.load(rk, (kt + 2) * BK);
-      vc.load(rv, (kt + 2) * BK);
+    if (nxt2 < nkt) {
+      kc.load(rk, nxt2 * BK);
+      vc.load(rv, nxt2 * BK);
     }
+    cur = nxt;
+    nxt = nxt2;
   }
 
   if (q < N) {
@@ -505,13 +550,15 @@ __device__ __forceinline__ void dq_body(
   }
 }
 
-template <typename T, int D, int NW, int BK, int OCC>
+template <typename T, int D, int NW, int BK, int OCC, bool BSP>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
-    int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len) {
-  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, BK>()];
-  dq_body<T, D, NW, BK>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2, kv_len);
+    int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
+    const uint8_t* __restrict__ bmask) {
+  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, BK, BSP>()];
+  dq_body<T, D, NW, BK, BSP>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2,
+                             kv_len, bmask);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -521,18 +568,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <typename T, int D>
+template <typename T, int D, bool BSP>
 __global__ __launch_bounds__(256, 2) void bwd_small_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ O, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ,
     T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal, float scale, float scale_log2,
-    const int32_t* __restrict__ kv_len, int nq) {
-  __shared__ __attribute__((aligned(16))) char smem[cmax(dq_lds_bytes<T, D, 32>(), dkdv_lds_bytes<T, D, 4, 64, true, false>())];
+    const int32_t* __restrict__ kv_len, int nq, const uint8_t* __restrict__ bmask) {
+  __shared__ __attribute__((aligned(16))) char
+      smem[cmax(dq_lds_bytes<T, D, 32, BSP>(), dkdv_lds_bytes<T, D, 4, 64, true, false, 1, BSP>())];
   if ((int)blockIdx.x < nq)
-    dq_body<T, D, 4, 32>(smem, blockIdx.x, Q, K, V, dO, O, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2, kv_len);
+    dq_body<T, D, 4, 32, BSP>(smem, blockIdx.x, Q, K, V, dO, O, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2,
+                              kv_len, bmask);
   else
-    dkdv_body<T, D, 4, 64, true, false>(smem, blockIdx.x - nq, Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal, scale,
-                                 scale_log2, kv_len);
+    dkdv_body<T, D, 4, 64, true, false, 1, BSP>(smem, blockIdx.x - nq, Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N,
+                                                causal, scale, scale_log2, kv_len, bmask);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -554,9 +603,14 @@ static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, 
   const int TK = (p.N + KT - 1) / KT;
   const int nlog = p.B * p.H * TK;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
-                     (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal, p.scale,
-                     p.scale * kLog2e, p.kv_len);
+  if (p.bmask)
+    hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                       (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal,
+                       p.scale, p.scale * kLog2e, p.kv_len, p.bmask);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, false>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                       (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal,
+                       p.scale, p.scale * kLog2e, p.kv_len, nullptr);
   return hipGetLastError();
 }
 
@@ -567,9 +621,14 @@ static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, co
   const int TQ = (p.N + QT - 1) / QT;
   const int nlog = p.B * p.H * TQ;
   const int grid = (nlog + 7) / 8 * 8;
-  hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q, (const T*)K,
-                     (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N, p.causal,
-                     p.scale, p.scale * kLog2e, p.kv_len);
+  if (p.bmask)
+    hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                       (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N,
+                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, p.bmask);
+  else
+    hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, false>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                       (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N,
+                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr);
   return hipGetLastError();
 }
 
@@ -582,9 +641,14 @@ static hipError_t launch_bwd_small_t(const Problem& p, const void* Q, const void
   const int BH = p.B * p.H;
   const int nq = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
   const int nk = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
-  hipLaunchKernelGGL((bwd_small_kernel<T, D>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
-                     (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
-                     p.scale, p.scale * kLog2e, p.kv_len, nq);
+  if (p.bmask)
+    hipLaunchKernelGGL((bwd_small_kernel<T, D, true>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
+                       (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
+                       p.scale, p.scale * kLog2e, p.kv_len, nq, p.bmask);
+  else
+    hipLaunchKernelGGL((bwd_small_kernel<T, D, false>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
+                       (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
+                       p.scale, p.scale * kLog2e, p.kv_len, nq, nullptr);
   return hipGetLastError();
 }
 

@@ -235,4 +235,49 @@ __device__ __forceinline__ int xcd_logical_block(int nlogical, int b) {
 }
 __device__ __forceinline__ int xcd_logical_block(int nlogical) { return xcd_logical_block(nlogical, blockIdx.x); }
 
+// ------------------------------------------------------------------------------------------
+// Block-sparse masks.  A mask is uint8 [TB][TB], TB = ceil(N / kMaskBlock), row-major, shared by
+// every (batch, head): entry (r, c) non-zero lets queries [64r, 64r + 64) attend keys
+// [64c, 64c + 64).  Every kernel tile lies inside one mask block along each dimension (tiles of
+// 32 or 64 rows, 64-aligned workgroup ranges), so each wave can skip a whole tile.
+constexpr int kMaskBlock = 64;
+constexpr int kMaxMaskBlocks = 1024;  // block-sparse calls need N <= 64 * kMaxMaskBlocks
+
+// A workgroup's view of the mask, one byte per mask block along the dimension it loops over:
+// bit j says whether the j-th mask block along its own dimension (j < 8) may meet that block.
+// `owned0` is the workgroup's first mask block along its own dimension, `nowned` how many it
+// spans; `by_row` selects whether the loop runs over mask columns (forward, dQ: the workgroup owns
+// query rows) or over mask rows (dK/dV: it owns key columns).
+__device__ __forceinline__ void build_tile_map(lds_t* map, const uint8_t* __restrict__ bmask, int tb, int owned0,
+                                               int nowned, bool by_row, int nthreads) {
+  for (int t = threadIdx.x; t < tb; t += nthreads) {
+    unsigned bits = 0;
+    for (int j = 0; j < nowned; ++j) {
+      const int o = owned0 + j;
+      if (o < tb) {
+        const uint8_t v = by_row ? bmask[(size_t)t * tb + o] : bmask[(size_t)o * tb + t];
+        bits |= (v != 0 ? 1u : 0u) << j;
+      }
+    }
+    reinterpret_cast<__attribute__((address_space(3))) uint8_t*>(map)[t] = (uint8_t)bits;
+  }
+}
+
+// Bits of the map entry for loop tile t (tiles of 64 >> shift rows along the loop dimension).
+__device__ __forceinline__ unsigned tile_bits(const lds_t* map, int t, int shift) {
+  return reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>(map)[t >> shift];
+}
+
+// Smallest loop tile index t in [from, end) whose map entry is non-zero, or end.  Each wave scans
+// 64 candidates per step with a ballot, so the answer is the same in every wave.
+__device__ __forceinline__ int next_live_tile(const lds_t* map, int from, int end, int shift) {
+  for (int base = from; base < end; base += 64) {
+    const int t = base + lane_id();
+    const bool live = t < end && tile_bits(map, t, shift) != 0;
+    const unsigned long long m = __ballot(live);
+    if (m) return base + __builtin_ctzll(m);
+  }
+  return end;
+}
+
 }  // namespace attn

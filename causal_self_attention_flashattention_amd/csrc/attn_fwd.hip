@@ -24,12 +24,13 @@ namespace attn {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int NW, int BK, int OCC>
+template <typename T, int D, int NW, int BK, int OCC, bool BSP>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, T* __restrict__ O,
                                                            float* __restrict__ Lse, int BH, int H, int N,
                                                            int causal, float scale_log2,
-                                                           const int32_t* __restrict__ kv_len) {
+                                                           const int32_t* __restrict__ kv_len,
+                                                           const uint8_t* __restrict__ bmask) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int QT = 32 * NW;             // queries per workgroup
@@ -39,11 +40,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   constexpr int NB = BK / 32;
   constexpr int LD = lds_pitch<T, DP>();  // LDS row stride (elements)
   constexpr int TILE = BK * LD * (int)sizeof(T);  // bytes of one K or V tile
+  constexpr int SHIFT = BK == 64 ? 0 : 1;          // key tiles per mask block = 1 << SHIFT
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
+  static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
+                "block-sparse tiles must nest in the 64 x 64 mask blocks");
 
-  // Two stages of (K tile, V tile): the next tile is written while the current one is read.
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  // Two stages of (K tile, V tile): the next tile is written while the current one is read; then,
+  // for block-sparse calls, one byte per mask column (which of this workgroup's rows see it).
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + (BSP ? kMaxMaskBlocks : 0)];
   lds_t* lds = (lds_t*)smem;
+  lds_t* map = lds + 4 * TILE;
 
   const int TQ = (N + QT - 1) / QT;
   const int logical = xcd_logical_block(BH * TQ);
@@ -66,6 +72,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   const bool wave_live = qw < N;
   // Last key this lane's query may see (the mask is "key > lim").
   const int lim = causal ? min(q, kv - 1) : kv - 1;
+  const unsigned wave_bit = 1u << ((32 * w) / kMaskBlock);  // this wave's mask row within the workgroup
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
@@ -90,22 +97,36 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
     zero_pad_cols<T, BK, D, LD, DP, NT>(lds + TILE);
     zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 3 * TILE);
   }
+  // Key tiles in loop order: all of [0, nkt), or (block-sparse) those some row of this workgroup
+  // may see; the current, next and next-but-one tiles are tracked for the two-stage pipeline.
+  int cur = 0;
+  if constexpr (BSP) {
+    build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
+    __syncthreads();
+    cur = next_live_tile(map, 0, nkt, SHIFT);
+  }
+  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, nkt, SHIFT) : t + 1; };
   TileCopy<T, BK, D, LD, NT> kc, vc;
-  kc.load(rk, 0);
-  vc.load(rv, 0);
-  kc.store(lds);
-  vc.store(lds + TILE);
+  if (cur < nkt) {
+    kc.load(rk, cur * BK);
+    vc.load(rv, cur * BK);
+    kc.store(lds);
+    vc.store(lds + TILE);
+  }
   __syncthreads();
-  if (nkt > 1) {
-    kc.load(rk, BK);
-    vc.load(rv, BK);
+  int nxt = cur < nkt ? after(cur) : nkt;
+  if (nxt < nkt) {
+    kc.load(rk, nxt * BK);
+    vc.load(rv, nxt * BK);
   }
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const lds_t* ktile = lds + (kt & 1) * 2 * TILE;
+  for (int it = 0; cur < nkt; ++it) {
+    const lds_t* ktile = lds + (it & 1) * 2 * TILE;
     const lds_t* vtile = ktile + TILE;
-    const int k0 = kt * BK;
-    if (wave_live && !(causal && k0 > qw_last)) {
+    const int k0 = cur * BK;
+    bool run = wave_live && !(causal && k0 > qw_last);
+    if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
+    if (run) {
       f32x16 s[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -156,20 +177,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
             o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
         }
     }
-    if (kt + 1 < nkt) {
-      lds_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
-      kc.store(nxt);
-      vc.store(nxt + TILE);
+    const int nxt2 = nxt < nkt ? after(nxt) : nkt;
+    if (nxt < nkt) {
+      lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
+      kc.store(st);
+      vc.store(st + TILE);
     }
     __syncthreads();
-    if (kt + 2 < nkt) {
-      kc.load(rk, (kt + 2) * BK);
-      vc.load(rv, (kt + 2) * BK);
+    if (nxt2 < nkt) {
+      kc.load(rk, nxt2 * BK);
+      vc.load(rv, nxt2 * BK);
     }
+    cur = nxt;
+    nxt = nxt2;
   }
 
   const float l_tot = l_part + swap_halves(l_part);
-  const float inv = 1.0f / l_tot;
+  // A block-sparse mask can leave a row without keys: O = 0 and L = -inf there.
+  const float inv = (BSP && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   if (q < N) {
     T* orow = O + (size_t)q * D;
 #pragma unroll
@@ -204,8 +229,12 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   const int nlog = p.B * p.H * TQ;
   const int grid = (nlog + 7) / 8 * 8;
   const float sl2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
-                     (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len);
+  if (p.bmask)
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
+                       (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len, p.bmask);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, false>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
+                       (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len, nullptr);
   return hipGetLastError();
 }
 

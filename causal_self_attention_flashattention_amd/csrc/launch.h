@@ -15,6 +15,7 @@ struct Problem {
   int causal;
   float scale;
   const int32_t* kv_len;  // device int32[B] or nullptr
+  const uint8_t* bmask;   // block-sparse mask, device uint8[TB][TB] (TB = ceil(N / 64)), or nullptr
 };
 
 bool fwd_supported(int dtype, int d);

@@ -96,6 +96,25 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, con
                 float* D, void* dQ, int B, int H, int N, int d, int causal, float scale, int dtype,
                 const int32_t* kv_len, hipStream_t stream);
 
+/* Block-sparse forward ("Notes on flashattention", section Block-sparse Flashattention): as
+ * attn_fwd, with the scores further restricted to the support of a mask that is constant on
+ * 64 x 64 blocks, and blocks outside it skipped entirely (neither loaded nor computed).
+ *   block_mask in: device uint8 [TB][TB], TB = ceil(N / 64), row-major, shared by every (batch,
+ *                  head); entry (r, c) != 0 lets queries 64r .. 64r+63 attend keys 64c .. 64c+63.
+ *                  Combined (AND) with the causal and key-padding masks.  NULL = attn_fwd.
+ * A query row left with no key at all gets O = 0 and L = -inf.  Requires N <= 65536
+ * (ATTN_E_SHAPE otherwise).  Outputs must not overlap any input, the mask included. */
+int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
+                         int d, int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
+                         hipStream_t stream);
+
+/* Block-sparse backward: attn_bwd under the same block mask as attn_fwd_blocksparse (O and L must
+ * come from that call).  Rows without keys get dQ = 0 and contribute nothing to dK, dV; D is
+ * still rowsum(O o dO).  NULL block_mask = attn_bwd.  Other arguments as for attn_bwd. */
+int attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                         void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                         int dtype, const int32_t* kv_len, const uint8_t* block_mask, hipStream_t stream);
+
 /* How many kernels attn_bwd launches for this problem: 1 when the dQ and dK/dV work share one
  * launch (small bfloat16 problems with d <= 80, where the grid would otherwise leave CUs idle),
  * 2 otherwise (attn_bwd_dq with O, then attn_bwd_dkdv).  Negative attn_status on bad arguments. */

@@ -55,6 +55,17 @@ def heads_to_numpy(t: torch.Tensor, heads):
     return out
 
 
+def d_slack(o_ref: np.ndarray, do, dtype: str) -> np.ndarray:
+    """Extra tolerance for D = rowsum(O o dO).  D is formed from the stored O, which the forward
+    rounds to the output dtype: in bfloat16 each O_c carries up to half an ulp (2^-9 relative) of
+    rounding on top of a computed error of the same order, so |dD_i| can reach
+    2^-8 * sum_c |O_ic dO_ic| even when O itself is within its tolerance.  float32: none."""
+    if dtype == "f32":
+        return np.zeros(o_ref.shape[:-1])
+    do = do.detach().double().cpu().numpy() if hasattr(do, "detach") else np.asarray(do, dtype=np.float64)
+    return 2.0 ** -8 * np.abs(o_ref * do).sum(-1)
+
+
 def oracle_ref(inputs: dict, causal: bool, scale: float, heads=None, with_bwd: bool = True):
     kv = inputs.get("kv_len")
     kv = None if kv is None else kv.tolist()
@@ -65,19 +76,22 @@ def oracle_ref(inputs: dict, causal: bool, scale: float, heads=None, with_bwd: b
         dq, dk, dv, dref = O.attention_backward(inputs["q"], inputs["k"], inputs["v"], inputs["do"], causal=causal,
                                                 scale=scale, kv_len=kv, heads=heads)
         ref.update(dQ=dq, dK=dk, dV=dv, D=dref)
+        ref["D_slack"] = d_slack(o, inputs["do"], "f32" if inputs["q"].dtype == torch.float32 else "bf16")
     return ref
 
 
-def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str):
-    """Assert the tolerance on every non-NaN reference element; return (max abs, max rel, worst index)."""
+def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str, slack=0.0):
+    """Assert the tolerance (plus ``slack``, broadcast like ref) on every non-NaN reference element;
+    return (max abs, max rel, worst index)."""
     sel = ~np.isnan(ref)
     g, r = got[sel], ref[sel]
+    sl = np.broadcast_to(slack, ref.shape)[sel]
     assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
     err = np.abs(g - r)
     if dtype == "f32":
-        bad = err > F32_ATOL
+        bad = err > F32_ATOL + sl
     else:
-        bad = err > BF16_ATOL + BF16_RTOL * np.abs(r)
+        bad = err > BF16_ATOL + BF16_RTOL * np.abs(r) + sl
     worst = int(np.argmax(err)) if err.size else 0
     stats = (float(err.max()) if err.size else 0.0,
              float((err / np.maximum(np.abs(r), 1e-6)).max()) if err.size else 0.0)
@@ -91,6 +105,9 @@ def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str):
 def compare_all(res: dict, ref: dict, dtype: str, heads):
     report = {}
     for key in ref:
+        if key == "D_slack":
+            continue
         got = heads_to_numpy(res[key], heads)
-        report[key] = check_close(key, got, ref[key], dtype)[0]
+        slack = ref.get("D_slack", 0.0) if key == "D" else 0.0
+        report[key] = check_close(key, got, ref[key], dtype, slack)[0]
     return report
