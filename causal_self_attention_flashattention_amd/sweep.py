@@ -97,13 +97,60 @@ def run_case(N: int, d: int, dtype: str, with_baseline: bool = True) -> dict:
     return row
 
 
+def blocksparse_case(B: int, H: int, N: int, d: int, density: float, seed: int = 0, pattern: str = "random") -> dict:
+    """Forward and backward time of causal block-sparse attention (bfloat16) next to the same
+    problem dense.  ``pattern`` "random": each 64 x 64 block kept with probability ``density``;
+    "band": a local band of blocks around the diagonal plus the first block column (global
+    tokens), its width chosen so that about ``density`` of the causal blocks are kept.  The
+    diagonal is always kept.  ``kept`` is the fraction of the causal (lower-triangle) blocks kept."""
+    import numpy as np
+
+    inp = make_inputs(B, H, N, d, "bf16", seed=seed)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    tb = attn.mask_blocks(N)
+    if pattern == "band":
+        width = max(1, int(round(density * (tb + 1) / 2)))
+        rr, cc = np.indices((tb, tb))
+        m = ((np.abs(rr - cc) < width) | (cc == 0)).astype(np.uint8)
+    else:
+        r = np.random.default_rng(seed)
+        m = (r.random((tb, tb)) < density).astype(np.uint8)
+    np.fill_diagonal(m, 1)
+    tri = np.tril(np.ones((tb, tb), dtype=bool))
+    kept = float(m[tri].sum()) / float(tri.sum())
+    bm = attn.block_mask_tensor(m, N, q.device)
+    row = {"B": B, "H": H, "N": N, "d": d, "density": density, "kept": kept, "pattern": pattern}
+    for tag, mask in (("dense", None), ("sparse", bm)):
+        o, L = attn.fwd(q, k, v, causal=True, block_mask=mask)
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(L))
+        row[tag + "_fwd_ms"] = _time(lambda: attn.fwd(q, k, v, causal=True, block_mask=mask, out=o, lse=L))
+        row[tag + "_bwd_ms"] = _time(lambda: attn.bwd(q, k, v, o, do, L, causal=True, block_mask=mask, outs=outs))
+    return row
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--quick", action="store_true", help="N in {2^7, 2^10, 2^13, 2^16} only")
     ap.add_argument("--json", action="store_true", help="one JSON object per case instead of a table")
     ap.add_argument("--no-baseline", action="store_true")
+    ap.add_argument("--blocksparse", action="store_true",
+                    help="instead: block-sparse timing against density (B=1, H=16, bf16, causal)")
     args = ap.parse_args()
     attn.load_library()
+    if args.blocksparse:
+        print("| pattern | N | d | causal blocks kept | dense fwd ms | sparse fwd ms | dense bwd ms | sparse bwd ms | "
+              "fwd+bwd speed-up |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for pattern in ("random", "band"):
+            for N in (4096, 16384):
+                for d in (64, 128):
+                    for dens in (0.5, 0.25, 0.125):
+                        r = blocksparse_case(1, 16, N, d, dens, pattern=pattern)
+                        sp = (r["dense_fwd_ms"] + r["dense_bwd_ms"]) / (r["sparse_fwd_ms"] + r["sparse_bwd_ms"])
+                        print(f"| {pattern} | {N} | {d} | {r['kept']:.3f} | {r['dense_fwd_ms']:.3f} | "
+                              f"{r['sparse_fwd_ms']:.3f} | {r['dense_bwd_ms']:.3f} | {r['sparse_bwd_ms']:.3f} | {sp:.2f}x |",
+                              flush=True)
+        return
     ns = [2 ** e for e in ((7, 10, 13, 16) if args.quick else range(7, 17))]
     if not args.json:
         print("| dtype | d | N | fwd ms | bwd ms | e2e ms | materialised fwd ms | materialised bwd ms | materialised e2e ms |")
