@@ -171,7 +171,7 @@ __device__ __forceinline__ void dkdv_body(
             part[h] = frag_dot(a, g, part[h]);
           }
         }
-        dself[r - qt0 * BQ] = part[0] + part[1];
+        dself[r - qt0 * BQ] = -(part[0] + part[1]);
       }
     }
 
@@ -183,7 +183,8 @@ __device__ __forceinline__ void dkdv_body(
     }
     TileCopy<T, BQ, D, LD, NT> qc, oc;
     // One staged value per thread: L (threads < BQ) or D (threads BQ..2BQ-1).  L is scaled to
-    // log2 units only when it is written to LDS, so that no arithmetic waits on the load here.
+    // log2 units and D negated only when written to LDS, so that no arithmetic waits on the load
+    // here.  -D is the initial value of the dP accumulator, which then yields dP - D directly.
     float lrd = 0.f;
     auto load_stage = [&](int qt) {
       qc.load(rq, qt * BQ);
@@ -197,7 +198,7 @@ __device__ __forceinline__ void dkdv_body(
       oc.store(st + TILE);
       if (threadIdx.x < (DSELF ? BQ : 2 * BQ))
         reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
-            threadIdx.x < BQ ? lrd * kLog2e : lrd;
+            threadIdx.x < BQ ? lrd * kLog2e : -lrd;
     };
     // Query tiles in loop order: all of [qt0, TQ), or (block-sparse) those whose mask row meets one
     // of this workgroup's key blocks; current, next and next-but-one are tracked for the pipeline.
@@ -230,9 +231,18 @@ __device__ __forceinline__ void dkdv_body(
         for (int qb = 0; qb < NQB; ++qb) {
           const int qb0 = q0 + qb * 32;
           if (qb0 >= N || (causal && qb0 + 31 < kw)) continue;  // past the end, or before this wave's keys
+          // dP accumulators start at -D of their rows (accumulator row order), so after the products
+          // they hold dP - D (eq. 17's bracket) with no further subtraction.
+          f32x16 nd;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nd[4 * m + r] = dd[r];
+          }
           f32x16 s[KB], dp[KB];
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+          for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = nd; }
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const typename M::frag qa = M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP);
@@ -267,7 +277,6 @@ __device__ __forceinline__ void dkdv_body(
           for (int m = 0; m < 4; ++m) {
             const int r0 = qb * 32 + 8 * m + 4 * half;
             const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lrow + r0);
-            const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + r0);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -275,7 +284,7 @@ __device__ __forceinline__ void dkdv_body(
                 const int e = 4 * m + r;
                 const float p = fast_exp2(__builtin_fmaf(s[kb][e], scale_log2, -lv[r]));
                 s[kb][e] = p;
-                dp[kb][e] = p * (dp[kb][e] - dd[r]);
+                dp[kb][e] = p * dp[kb][e];
               }
           }
 #pragma unroll
