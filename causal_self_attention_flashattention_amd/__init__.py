@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     bwd_dkdv,
     bwd_dq,
     fwd,
+    fwd_workspace_bytes,
     load_library,
     rowdot,
     status_string,
@@ -18,4 +19,4 @@ from .binding import (  # noqa: F401
 )
 from .function import FlashAttention, flash_attention  # noqa: F401
 
-__all__ = ["FlashAttention", "flash_attention", "fwd", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]
+__all__ = ["FlashAttention", "flash_attention", "fwd", "fwd_workspace_bytes", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

@@ -20,7 +20,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 # Names and C signatures of every exported entry point (kept in step with include/attn.h).
-_vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
@@ -30,6 +30,8 @@ SIGNATURES = {
     "attn_fwd_blocksparse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]),
     "attn_bwd_blocksparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                   _vp]),
+    "attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "attn_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
     "attn_bwd_launches": (_i, [_i, _i, _i, _i, _i]),
@@ -128,12 +130,20 @@ def block_mask_tensor(block_mask, N, device):
     return (m != 0).to(device=device, dtype=torch.uint8).contiguous()
 
 
+def fwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Workspace attn_fwd_ex can use for this shape (0 when the plain single launch is best)."""
+    return int(load_library().attn_fwd_workspace_bytes(B, H, N, d, _DTYPES[dtype]))
+
+
 def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, out=None, lse=None,
-        block_mask=None):
+        block_mask=None, workspace="auto"):
     """Attention forward. Returns ``(O, L)``: O like q, L float32 [B, H, N] (natural log).
 
     ``block_mask`` (optional, [ceil(N/64)]^2, non-zero = attend) restricts the scores to whole
-    64 x 64 blocks (block-sparse attention); masked blocks are skipped by the kernels."""
+    64 x 64 blocks (block-sparse attention); masked blocks are skipped by the kernels.
+    ``workspace``: "auto" allocates the scratch the library asks for (grids too small to fill the
+    chip then split each query tile's keys over several workgroups), None runs the plain single
+    launch, or pass a float32 CUDA tensor of at least ``fwd_workspace_bytes`` bytes."""
     B, H, N, d = _check_qkv(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
@@ -141,14 +151,13 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, o
     kv = kv_len_tensor(kv_len, B, q.device)
     bm = block_mask_tensor(block_mask, N, q.device)
     lib = load_library()
-    if bm is None:
-        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)), scale,
-                          _DTYPES[q.dtype], _ptr(kv), _stream())
-        _check("attn_fwd", st)
-    else:
-        st = lib.attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)),
-                                      scale, _DTYPES[q.dtype], _ptr(kv), _ptr(bm), _stream())
-        _check("attn_fwd_blocksparse", st)
+    if isinstance(workspace, str):
+        need = fwd_workspace_bytes(B, H, N, d, q.dtype)
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, H, N, d, int(bool(causal)), scale,
+                         _DTYPES[q.dtype], _ptr(kv), _ptr(bm), _ptr(workspace), ws_bytes, _stream())
+    _check("attn_fwd_ex", st)
     return o, L
 
 

@@ -84,19 +84,36 @@ const char* attn_status_string(int status) {
 
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,
              int causal, float scale, int dtype, const int32_t* kv_len, hipStream_t stream) {
+  return attn_fwd_ex(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, kv_len, nullptr, nullptr, 0, stream);
+}
+
+size_t attn_fwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_common(B, H, N, d, dtype, 1.0f, false) != ATTN_OK) return 0;
+  const attn::Problem p{B, H, N, d, 1, 1.0f, nullptr};
+  return attn::fwd_workspace_bytes(dtype, p);
+}
+
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,
+                int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!Q || !K || !V || !O || !L) return ATTN_E_NULL;
   int st = check_common(B, H, N, d, dtype, scale, true);
   if (st != ATTN_OK) return st;
+  if (block_mask && N > kMaxBlockSparseN) return ATTN_E_SHAPE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(L)) return ATTN_E_ALIGN;
+  if (workspace && !aligned16(workspace)) return ATTN_E_ALIGN;
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
   const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range outs[2] = {range_of(O, tb), range_of(L, lb)};
-  const Range ins[4] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb),
-                        kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}};
-  st = check_alias(outs, 2, ins, 4);
+  const size_t mb = block_mask ? (size_t)mask_blocks(N) * mask_blocks(N) : 0;
+  const Range outs[3] = {range_of(O, tb), range_of(L, lb),
+                         workspace ? range_of(workspace, workspace_bytes) : Range{0, 0}};
+  const Range ins[5] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb),
+                        kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}, range_of(block_mask, mb)};
+  st = check_alias(outs, workspace ? 3 : 2, ins, 5);
   if (st != ATTN_OK) return st;
-  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len};
-  if (attn::launch_fwd(dtype, p, Q, K, V, O, L, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
+  if (attn::launch_fwd(dtype, p, Q, K, V, O, L, stream, workspace, workspace ? workspace_bytes : 0) != hipSuccess)
+    return ATTN_E_LAUNCH;
   return ATTN_OK;
 }
 
@@ -149,23 +166,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
 int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
                          int d, int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
                          hipStream_t stream) {
-  if (!block_mask) return attn_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, kv_len, stream);
-  if (!Q || !K || !V || !O || !L) return ATTN_E_NULL;
-  int st = check_common(B, H, N, d, dtype, scale, true);
-  if (st != ATTN_OK) return st;
-  if (N > kMaxBlockSparseN) return ATTN_E_SHAPE;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(L)) return ATTN_E_ALIGN;
-  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const size_t mb = (size_t)mask_blocks(N) * mask_blocks(N);
-  const Range outs[2] = {range_of(O, tb), range_of(L, lb)};
-  const Range ins[5] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb),
-                        kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}, range_of(block_mask, mb)};
-  st = check_alias(outs, 2, ins, 5);
-  if (st != ATTN_OK) return st;
-  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
-  if (attn::launch_fwd(dtype, p, Q, K, V, O, L, stream) != hipSuccess) return ATTN_E_LAUNCH;
-  return ATTN_OK;
+  return attn_fwd_ex(Q, K, V, O, L, B, H, N, d, causal, scale, dtype, kv_len, block_mask, nullptr, 0, stream);
 }
 
 int attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,

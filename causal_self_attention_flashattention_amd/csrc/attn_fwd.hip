@@ -24,13 +24,18 @@ namespace attn {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int NW, int BK, int OCC, bool BSP>
+// With SPLIT the key range of every query tile is cut into `nsplit` chunks, one workgroup each;
+// a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
+// (layout: [nsplit][BH*N][D] floats, then [nsplit][BH*N][2] floats) instead of O and L, and
+// fwd_combine_kernel merges the chunks with Algorithm 1's rescaling.
+template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, T* __restrict__ O,
                                                            float* __restrict__ Lse, int BH, int H, int N,
                                                            int causal, float scale_log2,
                                                            const int32_t* __restrict__ kv_len,
-                                                           const uint8_t* __restrict__ bmask) {
+                                                           const uint8_t* __restrict__ bmask, int nsplit,
+                                                           float* __restrict__ part) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int QT = 32 * NW;             // queries per workgroup
@@ -52,10 +57,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   lds_t* map = lds + 4 * TILE;
 
   const int TQ = (N + QT - 1) / QT;
-  const int logical = xcd_logical_block(BH * TQ);
+  const int nsp = SPLIT ? nsplit : 1;
+  const int logical = xcd_logical_block(BH * TQ * nsp);
   if (logical < 0) return;
-  const int bh = logical / TQ;
-  const int qt = TQ - 1 - logical % TQ;  // heaviest (causal) tiles of a head first
+  const int split = logical % nsp;
+  const int bh = logical / nsp / TQ;
+  const int qt = TQ - 1 - logical / nsp % TQ;  // heaviest (causal) tiles of a head first
   const int b = bh / H;
   int kv = N;
   if (kv_len) kv = min(max(kv_len[b], 1), N);
@@ -77,6 +84,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
   const int nkt = (kend + BK - 1) / BK;
+  // This workgroup's key tiles [t_lo, t_hi): all of them, or one of nsplit equal chunks.
+  const int chunk = (nkt + nsp - 1) / nsp;
+  const int t_lo = SPLIT ? min(nkt, split * chunk) : 0;
+  const int t_hi = SPLIT ? min(nkt, t_lo + chunk) : nkt;
 
   const auto rq = make_rsrc(Q + base, (uint32_t)(N * D * sizeof(T)));
   const auto rk = make_rsrc(K + base, (uint32_t)(kend * D * sizeof(T)));  // keys >= kend read as 0
@@ -99,28 +110,28 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   }
   // Key tiles in loop order: all of [0, nkt), or (block-sparse) those some row of this workgroup
   // may see; the current, next and next-but-one tiles are tracked for the two-stage pipeline.
-  int cur = 0;
+  int cur = t_lo;
   if constexpr (BSP) {
     build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
     __syncthreads();
-    cur = next_live_tile(map, 0, nkt, SHIFT);
+    cur = next_live_tile(map, t_lo, t_hi, SHIFT);
   }
-  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, nkt, SHIFT) : t + 1; };
+  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
   TileCopy<T, BK, D, LD, NT> kc, vc;
-  if (cur < nkt) {
+  if (cur < t_hi) {
     kc.load(rk, cur * BK);
     vc.load(rv, cur * BK);
     kc.store(lds);
     vc.store(lds + TILE);
   }
   __syncthreads();
-  int nxt = cur < nkt ? after(cur) : nkt;
-  if (nxt < nkt) {
+  int nxt = cur < t_hi ? after(cur) : t_hi;
+  if (nxt < t_hi) {
     kc.load(rk, nxt * BK);
     vc.load(rv, nxt * BK);
   }
 
-  for (int it = 0; cur < nkt; ++it) {
+  for (int it = 0; cur < t_hi; ++it) {
     const lds_t* ktile = lds + (it & 1) * 2 * TILE;
     const lds_t* vtile = ktile + TILE;
     const int k0 = cur * BK;
@@ -177,14 +188,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
             o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
         }
     }
-    const int nxt2 = nxt < nkt ? after(nxt) : nkt;
-    if (nxt < nkt) {
+    const int nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+    if (nxt < t_hi) {
       lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
       kc.store(st);
       vc.store(st + TILE);
     }
     __syncthreads();
-    if (nxt2 < nkt) {
+    if (nxt2 < t_hi) {
       kc.load(rk, nxt2 * BK);
       vc.load(rv, nxt2 * BK);
     }
@@ -193,6 +204,31 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   }
 
   const float l_tot = l_part + swap_halves(l_part);
+  if constexpr (SPLIT) {
+    // Unnormalised partial: sum_j exp2(s_j - m) v_j, with m and sum_j exp2(s_j - m) beside it.
+    if (q < N) {
+      const size_t row = (size_t)split * BH * N + (size_t)bh * N + q;
+      float* prow = part + row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int d0 = db * 32 + 8 * m + 4 * half;
+          if (D % 32 == 0 || d0 < D) {
+            f32x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = o[db][4 * m + r];
+            *reinterpret_cast<f32x4*>(prow + d0) = v4;
+          }
+        }
+      if (half == 0) {
+        float* ml = part + (size_t)nsplit * BH * N * D + row * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+    return;
+  }
   // A block-sparse mask can leave a row without keys: O = 0 and L = -inf there.
   const float inv = (BSP && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
   if (q < N) {
@@ -221,21 +257,106 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   }
 }
 
+// Merge the nsplit partials of every row: with m = max_s m_s, O = sum_s 2^(m_s - m) O_s /
+// sum_s 2^(m_s - m) l_s and L = (m + log2 sum_s 2^(m_s - m) l_s) ln 2 -- the same rescaling
+// Algorithm 1 applies between key tiles.  Rows whose chunks saw no key give O = 0, L = -inf.
+// One thread per 4 consecutive columns of a row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ part, int nsplit, int rows,
+                                                          T* __restrict__ O, float* __restrict__ Lse) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int t = threadIdx.x;
+  if (t >= RPB * TPR) return;
+  const int row = blockIdx.x * RPB + t / TPR;
+  const int c = 4 * (t % TPR);
+  if (row >= rows) return;
+  const float* ml = part + (size_t)nsplit * rows * D;
+  float m = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ml[((size_t)sp * rows + row) * 2]);
+  float lsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (m > -INFINITY) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const size_t r = (size_t)sp * rows + row;
+      const float w = fast_exp2(ml[r * 2] - m);  // 0 for an empty chunk (its m is -inf)
+      lsum += w * ml[r * 2 + 1];
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + r * D + c);
+      acc += w * v;
+    }
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  T v4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v4[r] = (T)(acc[r] * inv);
+  if constexpr (sizeof(T) == 2) {
+    uint2 u;
+    __builtin_memcpy(&u, v4, 8);
+    *reinterpret_cast<uint2*>(O + (size_t)row * D + c) = u;
+  } else {
+    uint4 u;
+    __builtin_memcpy(&u, v4, 16);
+    *reinterpret_cast<uint4*>(O + (size_t)row * D + c) = u;
+  }
+  if (c == 0) Lse[row] = lsum > 0.f ? (m + fast_log2(lsum)) * kLn2 : -INFINITY;
+}
+
 template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O,
-                               float* L, hipStream_t stream) {
+                               float* L, hipStream_t stream, int nsplit = 1, float* part = nullptr) {
   constexpr int QT = 32 * NW;
   const int TQ = (p.N + QT - 1) / QT;
-  const int nlog = p.B * p.H * TQ;
-  const int grid = (nlog + 7) / 8 * 8;
   const float sl2 = p.scale * kLog2e;
+  const int BH = p.B * p.H;
+  if (nsplit > 1) {
+    const int grid = (BH * TQ * nsplit + 7) / 8 * 8;
+    if (p.bmask)
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true, true>), dim3(grid), dim3(NW * 64), 0, stream,
+                         (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
+                         p.bmask, nsplit, part);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, false, true>), dim3(grid), dim3(NW * 64), 0, stream,
+                         (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
+                         nullptr, nsplit, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int RPB = 256 / (D / 4);
+    const int rows = BH * p.N;
+    hipLaunchKernelGGL((fwd_combine_kernel<T, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
+                       (const float*)part, nsplit, rows, (T*)O, L);
+    return hipGetLastError();
+  }
+  const int grid = (BH * TQ + 7) / 8 * 8;
   if (p.bmask)
     hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
-                       (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len, p.bmask);
+                       (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len, p.bmask, 1,
+                       nullptr);
   else
     hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, false>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
-                       (const T*)K, (const T*)V, (T*)O, L, p.B * p.H, p.H, p.N, p.causal, sl2, p.kv_len, nullptr);
+                       (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len, nullptr, 1,
+                       nullptr);
   return hipGetLastError();
+}
+
+// Key chunks per query tile for the split forward.  Measured on MI355X: splitting pays when the
+// grid has fewer than ~4 query-tile workgroups per CU and the longest key chain is long (at least
+// 32 key tiles in bfloat16, 8 in float32, whose tiles cost about four times as much); below that
+// the partial writes and the merge launch cost more than they save (B=4, H=12, N=512 runs 1.6x
+// slower split).  Chunks hold at least four key tiles of the longest chain; at most kMaxSplits.
+int fwd_splits(int dtype, const Problem& p) {
+  const long items = (long)p.B * p.H * ((p.N + 127) / 128);
+  const int bk = dtype == kBF16 ? 64 : 32;
+  const int nkt_max = (p.N + bk - 1) / bk;
+  if (items >= 1024 || nkt_max < (dtype == kBF16 ? 32 : 8)) return 1;
+  int s = (int)((1280 + items - 1) / items);
+  s = s > kMaxSplits ? kMaxSplits : s;
+  s = s > nkt_max / 4 ? nkt_max / 4 : s;
+  return s >= 2 ? s : 1;
+}
+
+size_t fwd_workspace_bytes(int dtype, const Problem& p) {
+  const int s = fwd_splits(dtype, p);
+  return s > 1 ? (size_t)s * p.B * p.H * p.N * (p.d + 2) * sizeof(float) : 0;
 }
 
 bool fwd_supported(int dtype, int d) {
@@ -244,22 +365,26 @@ bool fwd_supported(int dtype, int d) {
 }
 
 hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K, const void* V, void* O,
-                      float* L, hipStream_t s) {
+                      float* L, hipStream_t s, void* workspace, size_t workspace_bytes) {
+  // The split path runs only with a workspace large enough for its partials.
+  const size_t need = fwd_workspace_bytes(dtype, p);
+  const int ns = (need > 0 && workspace && workspace_bytes >= need) ? fwd_splits(dtype, p) : 1;
+  float* part = (float*)workspace;
   if (dtype == kBF16) {
     switch (p.d) {
-      case 16: return launch_fwd_t<__bf16, 16, 4, 64, 2>(p, Q, K, V, O, L, s);
-      case 32: return launch_fwd_t<__bf16, 32, 4, 64, 2>(p, Q, K, V, O, L, s);
-      case 64: return launch_fwd_t<__bf16, 64, 4, 64, 2>(p, Q, K, V, O, L, s);
-      case 80: return launch_fwd_t<__bf16, 80, 4, 64, 2>(p, Q, K, V, O, L, s);
-      case 128: return launch_fwd_t<__bf16, 128, 4, 64, 2>(p, Q, K, V, O, L, s);
+      case 16: return launch_fwd_t<__bf16, 16, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      case 32: return launch_fwd_t<__bf16, 32, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      case 64: return launch_fwd_t<__bf16, 64, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      case 80: return launch_fwd_t<__bf16, 80, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      case 128: return launch_fwd_t<__bf16, 128, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
     }
   } else if (dtype == kF32) {
     switch (p.d) {
-      case 16: return launch_fwd_t<float, 16, 4, 32, 1>(p, Q, K, V, O, L, s);
-      case 32: return launch_fwd_t<float, 32, 4, 32, 1>(p, Q, K, V, O, L, s);
-      case 64: return launch_fwd_t<float, 64, 4, 32, 1>(p, Q, K, V, O, L, s);
-      case 80: return launch_fwd_t<float, 80, 4, 32, 1>(p, Q, K, V, O, L, s);
-      case 128: return launch_fwd_t<float, 128, 4, 32, 1>(p, Q, K, V, O, L, s);
+      case 16: return launch_fwd_t<float, 16, 4, 32, 1>(p, Q, K, V, O, L, s, ns, part);
+      case 32: return launch_fwd_t<float, 32, 4, 32, 1>(p, Q, K, V, O, L, s, ns, part);
+      case 64: return launch_fwd_t<float, 64, 4, 32, 1>(p, Q, K, V, O, L, s, ns, part);
+      case 80: return launch_fwd_t<float, 80, 4, 32, 1>(p, Q, K, V, O, L, s, ns, part);
+      case 128: return launch_fwd_t<float, 128, 4, 32, 1>(p, Q, K, V, O, L, s, ns, part);
     }
   }
   return hipErrorInvalidValue;

@@ -21,8 +21,14 @@ struct Problem {
 bool fwd_supported(int dtype, int d);
 bool bwd_supported(int dtype, int d);
 
+// Forward.  With a workspace of at least fwd_workspace_bytes(dtype, p) bytes (non-zero only for
+// grids too small to fill the chip) the key range of every query tile is split over several
+// workgroups whose partial results a second kernel merges; otherwise one launch.
+constexpr int kMaxSplits = 16;
 hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
-                      void* O, float* L, hipStream_t stream);
+                      void* O, float* L, hipStream_t stream, void* workspace = nullptr, size_t workspace_bytes = 0);
+int fwd_splits(int dtype, const Problem& p);
+size_t fwd_workspace_bytes(int dtype, const Problem& p);
 
 hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void* dO, float* Dv,
                          hipStream_t stream);

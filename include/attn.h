@@ -30,6 +30,7 @@
 #define ATTN_H_
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -107,6 +108,22 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, con
 int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
                          int d, int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
                          hipStream_t stream);
+
+/* Bytes of workspace attn_fwd_ex can use for this shape: non-zero when B*H*ceil(N/128) query
+ * tiles are too few to fill the chip, in which case the key range of each query tile is split
+ * over several workgroups (partial results in the workspace, merged by a second kernel with the
+ * online-softmax rescaling of the handout's Algorithm 1).  0 on bad arguments. */
+size_t attn_fwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/* attn_fwd with every option: block_mask as for attn_fwd_blocksparse (NULL = none), and a
+ * caller-owned device workspace.  With workspace_bytes >= attn_fwd_workspace_bytes(...) the split
+ * path runs; with a smaller (or NULL) workspace the plain single launch runs.  The results agree
+ * with attn_fwd to rounding (the split sums in a different order); both are deterministic.  The
+ * workspace must be 16-byte aligned and must not overlap any input or output; its contents are
+ * scratch (not read before written). */
+int attn_fwd_ex(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,
+                int causal, float scale, int dtype, const int32_t* kv_len, const uint8_t* block_mask,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Block-sparse backward: attn_bwd under the same block mask as attn_fwd_blocksparse (O and L must
  * come from that call).  Rows without keys get dQ = 0 and contribute nothing to dK, dV; D is

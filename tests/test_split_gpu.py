@@ -1,0 +1,101 @@
+"""Split-key forward (attn_fwd_ex with a workspace): for grids too small to fill the chip the key
+range of each query tile is cut into chunks on separate workgroups, and a second kernel merges the
+partial (max, sum, unnormalised O) triples with the online-softmax rescaling of the hand-out's
+Algorithm 1.  Both the split and the plain path are compared with the float64 oracle on shapes
+where the split is planned, including key padding, block-sparse masks with keyless rows, and
+sequences shorter than one chunk per split."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as ref
+from causal_self_attention_flashattention_amd import binding as attn
+from causal_self_attention_flashattention_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _close(name, got, want, dtype):
+    a, r = (1e-4, 0.0) if dtype == "f32" else (2e-2, 1e-2)
+    got = got.detach().double().cpu().numpy()
+    inf = np.isinf(want)
+    assert np.array_equal(np.isinf(got), inf), f"{name}: -inf pattern differs"
+    err = np.abs(got[~inf] - want[~inf])
+    bound = a + r * np.abs(want[~inf])
+    assert np.all(err <= bound), f"{name}: max err {err.max():.3g}, worst ratio {(err / bound).max():.3g}"
+
+
+CASES = [
+    # B, H, N, d, dtype, causal, kv_len, block-mask density (None = dense), split planned
+    (1, 1, 4096, 64, "bf16", True, None, None, True),
+    (1, 1, 3000, 128, "bf16", False, None, None, True),
+    (1, 2, 2100, 80, "bf16", True, [1900], None, True),
+    (2, 1, 777, 16, "f32", True, None, None, True),
+    (1, 1, 2048, 32, "f32", False, [1500], None, True),
+    (1, 1, 300, 64, "f32", True, None, None, True),
+    (1, 1, 1000, 64, "bf16", True, None, None, False),
+    (4, 12, 512, 64, "bf16", True, None, None, False),
+    (1, 1, 1, 128, "f32", True, None, None, False),
+    (1, 2, 2500, 64, "bf16", True, None, 0.3, True),
+    (1, 1, 1500, 128, "f32", False, [1400], 0.4, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,kv,density,planned", CASES)
+def test_split_forward_matches_oracle(B, H, N, d, dtype, causal, kv, density, planned):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert (attn.fwd_workspace_bytes(B, H, N, d, tdt) > 0) == planned
+    inp = make_inputs(B, H, N, d, dtype, seed=50 + N, kv_len=kv)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    kvd = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+    bm = None
+    if density is not None:
+        tb = attn.mask_blocks(N)
+        bm = (np.random.default_rng(N).random((tb, tb)) < density).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+        bm[1, :] = 0  # query block 1 sees no key
+    scale = 1.0 / math.sqrt(d)
+    o_s, l_s = attn.fwd(q, k, v, causal=causal, scale=scale, kv_len=kvd, block_mask=bm, workspace="auto")
+    o_p, l_p = attn.fwd(q, k, v, causal=causal, scale=scale, kv_len=kvd, block_mask=bm, workspace=None)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal, scale=scale, kv_len=kv,
+                                   block_mask=bm, block=64)
+    for b in range(B):
+        for h in range(H):
+            for tag, o, l in (("split", o_s, l_s), ("plain", o_p, l_p)):
+                _close(f"O {tag} (b={b}, h={h})", o[b, h], ro[b, h], dtype)
+                _close(f"L {tag} (b={b}, h={h})", l[b, h], rl[b, h], dtype)
+
+
+def test_split_forward_feeds_backward():
+    # O and L from the split forward drive the backward to the same gradients (within tolerance).
+    B, H, N, d = 1, 2, 1536, 64
+    inp = make_inputs(B, H, N, d, "bf16", seed=9)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    o, L = attn.fwd(q, k, v, causal=True, workspace="auto")
+    dq, dk, dv, _ = attn.bwd(q, k, v, o, do, L, causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = ref.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True, scale=1 / 8)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        for h in range(H):
+            _close(f"{name} h={h}", g[0, h], r[0, h], "bf16")
+
+
+def test_small_workspace_falls_back_to_one_launch():
+    inp = make_inputs(1, 1, 2048, 64, "bf16", seed=4)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    need = attn.fwd_workspace_bytes(1, 1, 2048, 64, torch.bfloat16)
+    small = torch.empty(need // 8, dtype=torch.float32, device="cuda")
+    o1, l1 = attn.fwd(q, k, v, workspace=small)
+    o2, l2 = attn.fwd(q, k, v, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_large_grids_plan_no_split():
+    assert attn.fwd_workspace_bytes(4, 20, 4096, 64, torch.bfloat16) == 0
+    assert attn.fwd_workspace_bytes(1, 36, 16384, 128, torch.bfloat16) == 0
+    assert attn.fwd_workspace_bytes(4, 32, 2048, 80, torch.bfloat16) == 0
