@@ -7,6 +7,7 @@ The computation lives in ``libattn.so`` (HIP kernels for gfx950 behind a C ABI, 
 from .binding import (  # noqa: F401
     AttnError,
     bwd,
+    bwd_workspace_bytes,
     bwd_launches,
     bwd_dkdv,
     bwd_dq,
@@ -19,4 +20,4 @@ from .binding import (  # noqa: F401
 )
 from .function import FlashAttention, flash_attention  # noqa: F401
 
-__all__ = ["FlashAttention", "flash_attention", "fwd", "fwd_workspace_bytes", "bwd", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]
+__all__ = ["FlashAttention", "flash_attention", "fwd", "fwd_workspace_bytes", "bwd", "bwd_workspace_bytes", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

@@ -32,6 +32,9 @@ SIGNATURES = {
                                   _vp]),
     "attn_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "attn_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
+    "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "attn_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp,
+                         _sz, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
     "attn_bwd_launches": (_i, [_i, _i, _i, _i, _i]),
@@ -161,10 +164,16 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, o
     return o, L
 
 
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Workspace attn_bwd_ex can use for this shape (0 when the plain launches are best)."""
+    return int(load_library().attn_bwd_workspace_bytes(B, H, N, d, _DTYPES[dtype]))
+
+
 def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv_len=None, outs=None,
-        block_mask=None):
+        block_mask=None, workspace="auto"):
     """Attention backward. Returns ``(dQ, dK, dV, D)``; D = rowsum(O o dO) float32 [B, H, N].
-    ``block_mask`` as for :func:`fwd` (the same mask the forward used)."""
+    ``block_mask`` as for :func:`fwd` (the same mask the forward used); ``workspace`` as for
+    :func:`fwd` (``bwd_workspace_bytes``)."""
     B, H, N, d = _check_qkv(q, k, v, o, do)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if outs is None:
@@ -174,16 +183,14 @@ def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv
         dq, dk, dv, D = outs
     kv = kv_len_tensor(kv_len, B, q.device)
     bm = block_mask_tensor(block_mask, N, q.device)
-    lib = load_library()
-    if bm is None:
-        st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype], _ptr(kv), _stream())
-        _check("attn_bwd", st)
-    else:
-        st = lib.attn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                                      _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
-                                      _ptr(kv), _ptr(bm), _stream())
-        _check("attn_bwd_blocksparse", st)
+    if isinstance(workspace, str):
+        need = bwd_workspace_bytes(B, H, N, d, q.dtype)
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
+                                    _ptr(kv), _ptr(bm), _ptr(workspace), ws_bytes, _stream())
+    _check("attn_bwd_ex", st)
     return dq, dk, dv, D
 
 

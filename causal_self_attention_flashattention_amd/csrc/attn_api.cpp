@@ -136,30 +136,54 @@ int attn_bwd_rowdot(const void* O, const void* dO, float* D, int B, int H, int N
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
              void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
              int dtype, const int32_t* kv_len, hipStream_t stream) {
+  return attn_bwd_ex(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, causal, scale, dtype, kv_len, nullptr, nullptr, 0,
+                     stream);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_common(B, H, N, d, dtype, 1.0f, false) != ATTN_OK) return 0;
+  const attn::Problem p{B, H, N, d, 1, 1.0f, nullptr};
+  return attn::bwd_workspace_bytes(dtype, p);
+}
+
+int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                int dtype, const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
   if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !D) return ATTN_E_NULL;
   int st = check_common(B, H, N, d, dtype, scale, true);
   if (st != ATTN_OK) return st;
+  if (block_mask && N > kMaxBlockSparseN) return ATTN_E_SHAPE;
   const void* ptrs[] = {Q, K, V, O, dO, L, dQ, dK, dV, D};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_E_ALIGN;
+  if (workspace && !aligned16(workspace)) return ATTN_E_ALIGN;
   const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
   const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range outs[4] = {range_of(dQ, tb), range_of(dK, tb), range_of(dV, tb), range_of(D, lb)};
-  const Range ins[7] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(O, tb),
-                        range_of(dO, tb), range_of(L, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0}};
-  st = check_alias(outs, 4, ins, 7);
+  const size_t mb = block_mask ? (size_t)mask_blocks(N) * mask_blocks(N) : 0;
+  const Range outs[5] = {range_of(dQ, tb), range_of(dK, tb), range_of(dV, tb), range_of(D, lb),
+                         workspace ? range_of(workspace, workspace_bytes) : Range{0, 0}};
+  const Range ins[8] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(O, tb), range_of(dO, tb),
+                        range_of(L, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0},
+                        range_of(block_mask, mb)};
+  st = check_alias(outs, workspace ? 5 : 4, ins, 8);
   if (st != ATTN_OK) return st;
-  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len};
-  if (attn::bwd_small_applies(dtype, p)) {
+  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
+  const size_t need = attn::bwd_workspace_bytes(dtype, p);
+  const bool split = need > 0 && workspace && workspace_bytes >= need;
+  if (!split && attn::bwd_small_applies(dtype, p)) {
     // Small grids: dQ and dK/dV side by side in one launch.
     if (attn::launch_bwd_small(dtype, p, Q, K, V, dO, O, L, D, dQ, dK, dV, stream) != hipSuccess)
       return ATTN_E_LAUNCH;
     return ATTN_OK;
   }
   // The dQ kernel computes D for its query rows on the way (replacing the separate pre-pass), so it
-  // runs first; the dK/dV kernel then reads D.
-  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
-  if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream) != hipSuccess) return ATTN_E_LAUNCH;
+  // runs first; the dK/dV kernel then reads D.  With a large enough workspace both split their
+  // workgroup chains (the two phases reuse the workspace one after the other).
+  void* ws = split ? workspace : nullptr;
+  const size_t wb = split ? workspace_bytes : 0;
+  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream, ws, wb) != hipSuccess) return ATTN_E_LAUNCH;
+  if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream, ws, wb) != hipSuccess) return ATTN_E_LAUNCH;
   return ATTN_OK;
 }
 
@@ -172,33 +196,8 @@ int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, f
 int attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
                          void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
                          int dtype, const int32_t* kv_len, const uint8_t* block_mask, hipStream_t stream) {
-  if (!block_mask)
-    return attn_bwd(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, causal, scale, dtype, kv_len, stream);
-  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !D) return ATTN_E_NULL;
-  int st = check_common(B, H, N, d, dtype, scale, true);
-  if (st != ATTN_OK) return st;
-  if (N > kMaxBlockSparseN) return ATTN_E_SHAPE;
-  const void* ptrs[] = {Q, K, V, O, dO, L, dQ, dK, dV, D};
-  for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return ATTN_E_ALIGN;
-  const size_t tb = (size_t)B * H * N * d * elem_size(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const size_t mb = (size_t)mask_blocks(N) * mask_blocks(N);
-  const Range outs[4] = {range_of(dQ, tb), range_of(dK, tb), range_of(dV, tb), range_of(D, lb)};
-  const Range ins[8] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(O, tb), range_of(dO, tb),
-                        range_of(L, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0},
-                        range_of(block_mask, mb)};
-  st = check_alias(outs, 4, ins, 8);
-  if (st != ATTN_OK) return st;
-  const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
-  if (attn::bwd_small_applies(dtype, p)) {
-    if (attn::launch_bwd_small(dtype, p, Q, K, V, dO, O, L, D, dQ, dK, dV, stream) != hipSuccess)
-      return ATTN_E_LAUNCH;
-    return ATTN_OK;
-  }
-  if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream) != hipSuccess) return ATTN_E_LAUNCH;
-  if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream) != hipSuccess) return ATTN_E_LAUNCH;
-  return ATTN_OK;
+  return attn_bwd_ex(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, causal, scale, dtype, kv_len, block_mask, nullptr,
+                     0, stream);
 }
 
 int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,

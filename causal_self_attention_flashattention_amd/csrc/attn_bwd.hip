@@ -71,13 +71,16 @@ constexpr int dkdv_lds_bytes() {
 // workgroup's V rows are kept in LDS and read per block instead of being held in registers (frees
 // 32 VGPRs per key block at d = 128, where the register file is otherwise too small).  With BSP
 // the query tiles whose mask row meets none of the workgroup's key blocks are skipped, and each
-// wave skips the tiles its own mask block excludes.
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false>
+// wave skips the tiles its own mask block excludes.  With SPLIT the query tiles of every key tile
+// are cut into `nsplit` chunks, one workgroup each, which write unscaled float32 partial dK and dV
+// rows to `part` ([nsplit][BH*N][D] for dK, then the same for dV) for bwd_sum_kernel to add up.
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, bool SPLIT = false>
 __device__ __forceinline__ void dkdv_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
     const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal,
-    float scale, float scale_log2, const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask) {
+    float scale, float scale_log2, const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask,
+    int nsplit = 1, float* __restrict__ part = nullptr) {
   using M = Mfma<T>;
   constexpr int NT = NW * 64;
   constexpr int KW = 32 * KB;  // keys per wave
@@ -98,10 +101,12 @@ __device__ __forceinline__ void dkdv_body(
   lds_t* map = lds + dkdv_lds_bytes<T, D, NW, BQ, DSELF, VLDS, KB, false>();
 
   const int TK = (N + KT - 1) / KT;
-  const int logical = xcd_logical_block(BH * TK, block);
+  const int nsp = SPLIT ? nsplit : 1;
+  const int logical = xcd_logical_block(BH * TK * nsp, block);
   if (logical < 0) return;
-  const int bh = logical / TK;
-  const int kt = logical % TK;  // low key tiles see the most queries under causal masking
+  const int split = logical % nsp;
+  const int bh = logical / nsp / TK;
+  const int kt = logical / nsp % TK;  // low key tiles see the most queries under causal masking
   const int b = bh / H;
   int kv = N;
   if (kv_len) kv = min(max(kv_len[b], 1), N);
@@ -152,6 +157,10 @@ __device__ __forceinline__ void dkdv_body(
       }
     const int TQ = (N + BQ - 1) / BQ;
     const int qt0 = causal ? k0 / BQ : 0;
+    // This workgroup's query tiles [qt_lo, qt_hi): all from qt0, or one of nsplit equal chunks.
+    const int qchunk = (TQ - qt0 + nsp - 1) / nsp;
+    const int qt_lo = SPLIT ? min(TQ, qt0 + split * qchunk) : qt0;
+    const int qt_hi = SPLIT ? min(TQ, qt_lo + qchunk) : TQ;
 
     // DSELF: D for rows [qt0*BQ, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
@@ -202,22 +211,22 @@ __device__ __forceinline__ void dkdv_body(
     };
     // Query tiles in loop order: all of [qt0, TQ), or (block-sparse) those whose mask row meets one
     // of this workgroup's key blocks; current, next and next-but-one are tracked for the pipeline.
-    int cur = qt0;
+    int cur = qt_lo;
     if constexpr (BSP) {
       build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, k0 / kMaskBlock, KT / kMaskBlock, true, NT);
       __syncthreads();
-      cur = next_live_tile(map, qt0, TQ, SHIFT);
+      cur = next_live_tile(map, qt_lo, qt_hi, SHIFT);
     }
-    auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, TQ, SHIFT) : t + 1; };
-    if (cur < TQ) {
+    auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, qt_hi, SHIFT) : t + 1; };
+    if (cur < qt_hi) {
       load_stage(cur);
       store_stage(lds);
     }
     __syncthreads();
-    int nxt = cur < TQ ? after(cur) : TQ;
-    if (nxt < TQ) load_stage(nxt);
+    int nxt = cur < qt_hi ? after(cur) : qt_hi;
+    if (nxt < qt_hi) load_stage(nxt);
 
-    for (int it = 0; cur < TQ; ++it) {
+    for (int it = 0; cur < qt_hi; ++it) {
       const int q0 = cur * BQ;
       const lds_t* qtile = lds + (it & 1) * STAGE;
       const lds_t* otile = qtile + TILE;
@@ -308,15 +317,43 @@ __device__ __forceinline__ void dkdv_body(
           }
         }
       }
-      const int nxt2 = nxt < TQ ? after(nxt) : TQ;
-      if (nxt < TQ) store_stage(lds + ((it + 1) & 1) * STAGE);
+      const int nxt2 = nxt < qt_hi ? after(nxt) : qt_hi;
+      if (nxt < qt_hi) store_stage(lds + ((it + 1) & 1) * STAGE);
       __syncthreads();
-      if (nxt2 < TQ) load_stage(nxt2);
+      if (nxt2 < qt_hi) load_stage(nxt2);
       cur = nxt;
       nxt = nxt2;
     }
   }
 
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = kw + 32 * kb + col;
+      if (key < N) {
+        const size_t row = (size_t)split * BH * N + (size_t)bh * N + key;
+        float* prk = part + row * D;
+        float* prv = part + (size_t)nsplit * BH * N * D + row * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int d0 = db * 32 + 8 * m + 4 * half;
+            if (D % 32 == 0 || d0 < D) {
+              f32x4 k4, v4;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                k4[r] = dk[kb][db][4 * m + r];
+                v4[r] = dv[kb][db][4 * m + r];
+              }
+              *reinterpret_cast<f32x4*>(prk + d0) = k4;
+              *reinterpret_cast<f32x4*>(prv + d0) = v4;
+            }
+          }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw + 32 * kb + col;
@@ -354,15 +391,15 @@ __device__ __forceinline__ void dkdv_body(
   }
 }
 
-template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB, bool BSP>
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB, bool BSP, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
     int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
-    const uint8_t* __restrict__ bmask) {
+    const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB, BSP>()];
-  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH, H, N,
-                                                causal, scale, scale_log2, kv_len, bmask);
+  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP, SPLIT>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH,
+                                                       H, N, causal, scale, scale_log2, kv_len, bmask, nsplit, part);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -374,12 +411,13 @@ constexpr int dq_lds_bytes() {
   return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T) + (BSP ? kMaxMaskBlocks : 0);
 }
 
-template <typename T, int D, int NW, int BK, bool BSP = false>
+template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false>
 __device__ __forceinline__ void dq_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
     T* __restrict__ dQ, int BH, int H, int N, int causal, float scale, float scale_log2,
-    const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask) {
+    const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask, int nsplit = 1,
+    float* __restrict__ part = nullptr) {
   // With Oin != nullptr the kernel first computes D = rowsum(O o dO) for its own query rows (each
   // row belongs to exactly one workgroup) and stores it to Dv for the dK/dV kernel that follows;
   // otherwise it reads D from Dv.
@@ -400,10 +438,12 @@ __device__ __forceinline__ void dq_body(
   lds_t* map = lds + 4 * TILE;
 
   const int TQ = (N + QT - 1) / QT;
-  const int logical = xcd_logical_block(BH * TQ, block);
+  const int nsp = SPLIT ? nsplit : 1;
+  const int logical = xcd_logical_block(BH * TQ * nsp, block);
   if (logical < 0) return;
-  const int bh = logical / TQ;
-  const int qt = TQ - 1 - logical % TQ;
+  const int split = logical % nsp;
+  const int bh = logical / nsp / TQ;
+  const int qt = TQ - 1 - logical / nsp % TQ;
   const int b = bh / H;
   int kv = N;
   if (kv_len) kv = min(max(kv_len[b], 1), N);
@@ -423,6 +463,11 @@ __device__ __forceinline__ void dq_body(
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
   const int nkt = (kend + BK - 1) / BK;
+  // This workgroup's key tiles [t_lo, t_hi): all of them, or one of nsplit equal chunks (SPLIT:
+  // unscaled float32 partial dQ rows go to part, [nsplit][BH*N][D], for bwd_sum_kernel).
+  const int chunk = (nkt + nsp - 1) / nsp;
+  const int t_lo = SPLIT ? min(nkt, split * chunk) : 0;
+  const int t_hi = SPLIT ? min(nkt, t_lo + chunk) : nkt;
 
   const uint32_t tbytes = (uint32_t)(N * D * sizeof(T));
   const auto rq = make_rsrc(Q + base, tbytes);
@@ -440,11 +485,11 @@ __device__ __forceinline__ void dq_body(
   float dq_;
   if (Oin) {
     const auto rO = make_rsrc(Oin + base, tbytes);
-    float part = 0.f;
+    float dpart = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) part = frag_dot(frag_global<T>(rO, q, D, ks * M::KSTEP), of[ks], part);
-    dq_ = part + swap_halves(part);
-    if (half == 0 && q < N) Dv[(size_t)bh * N + q] = dq_;
+    for (int ks = 0; ks < KS; ++ks) dpart = frag_dot(frag_global<T>(rO, q, D, ks * M::KSTEP), of[ks], dpart);
+    dq_ = dpart + swap_halves(dpart);
+    if (half == 0 && q < N && split == 0) Dv[(size_t)bh * N + q] = dq_;
   } else {
     dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
   }
@@ -465,27 +510,27 @@ __device__ __forceinline__ void dq_body(
     zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 2 * TILE);
   }
   // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
-  int cur = 0;
+  int cur = t_lo;
   if constexpr (BSP) {
     build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
     __syncthreads();
-    cur = next_live_tile(map, 0, nkt, SHIFT);
+    cur = next_live_tile(map, t_lo, t_hi, SHIFT);
   }
-  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, nkt, SHIFT) : t + 1; };
+  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
   TileCopy<T, BK, D, LD, NT> kc, vc;
-  if (cur < nkt) {
+  if (cur < t_hi) {
     kc.load(rk, cur * BK);
     vc.load(rv, cur * BK);
     kc.store(lds);
     vc.store(lds + TILE);
   }
   __syncthreads();
-  int nxt = cur < nkt ? after(cur) : nkt;
-  if (nxt < nkt) {
+  int nxt = cur < t_hi ? after(cur) : t_hi;
+  if (nxt < t_hi) {
     kc.load(rk, nxt * BK);
     vc.load(rv, nxt * BK);
   }
-  for (int it = 0; cur < nkt; ++it) {
+  for (int it = 0; cur < t_hi; ++it) {
     const lds_t* ktile = lds + (it & 1) * 2 * TILE;
     const lds_t* vtile = ktile + TILE;
     bool run = wave_live;
@@ -519,14 +564,14 @@ __device__ __forceinline__ void dq_body(
         }
       }
     }
-    const int nxt2 = nxt < nkt ? after(nxt) : nkt;
-    if (nxt < nkt) {
+    const int nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+    if (nxt < t_hi) {
       lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
       kc.store(st);
       vc.store(st + TILE);
     }
     __syncthreads();
-    if (nxt2 < nkt) {
+    if (nxt2 < t_hi) {
       kc.load(rk, nxt2 * BK);
       vc.load(rv, nxt2 * BK);
     }
@@ -534,6 +579,24 @@ __device__ __forceinline__ void dq_body(
     nxt = nxt2;
   }
 
+  if constexpr (SPLIT) {
+    if (q < N) {
+      float* prow = part + ((size_t)split * BH * N + (size_t)bh * N + q) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int d0 = db * 32 + 8 * m + 4 * half;
+          if (D % 32 == 0 || d0 < D) {
+            f32x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = acc[db][4 * m + r];
+            *reinterpret_cast<f32x4*>(prow + d0) = v4;
+          }
+        }
+    }
+    return;
+  }
   if (q < N) {
     T* row = dQ + (size_t)q * D;
 #pragma unroll
@@ -559,15 +622,45 @@ __device__ __forceinline__ void dq_body(
   }
 }
 
-template <typename T, int D, int NW, int BK, int OCC, bool BSP>
+template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
     int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
-    const uint8_t* __restrict__ bmask) {
+    const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, BK, BSP>()];
-  dq_body<T, D, NW, BK, BSP>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale, scale_log2,
-                             kv_len, bmask);
+  dq_body<T, D, NW, BK, BSP, SPLIT>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale,
+                                    scale_log2, kv_len, bmask, nsplit, part);
+}
+
+// out = scale * sum_s part[s] elementwise (fixed order, so the split backward stays deterministic),
+// converted to the output dtype; 4 elements per thread (count is a multiple of 4).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_sum_kernel(const float* __restrict__ part, int nsplit, size_t count,
+                                                      float scale, T* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int sp = 1; sp < nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * count + i);
+  T v4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v4[r] = (T)(acc[r] * scale);
+  if constexpr (sizeof(T) == 2) {
+    uint2 u;
+    __builtin_memcpy(&u, v4, 8);
+    *reinterpret_cast<uint2*>(out + i) = u;
+  } else {
+    uint4 u;
+    __builtin_memcpy(&u, v4, 16);
+    *reinterpret_cast<uint4*>(out + i) = u;
+  }
+}
+
+template <typename T>
+static hipError_t launch_sum(const float* part, int nsplit, size_t count, float scale, void* out, hipStream_t s) {
+  const unsigned blocks = (unsigned)((count / 4 + 255) / 256);
+  hipLaunchKernelGGL((bwd_sum_kernel<T>), dim3(blocks), dim3(256), 0, s, part, nsplit, count, scale, (T*)out);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -607,37 +700,72 @@ static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* d
 
 template <typename T, int D, int NW, int BQ, int OCC, bool VLDS = false, int KB = 1>
 static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                                const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
+                                const float* L, const float* Dv, void* dK, void* dV, hipStream_t s, int nsplit,
+                                float* part) {
   constexpr int KT = 32 * KB * NW;
   const int TK = (p.N + KT - 1) / KT;
-  const int nlog = p.B * p.H * TK;
+  const int BH = p.B * p.H;
+  if (nsplit > 1) {
+    const int grid = (BH * TK * nsplit + 7) / 8 * 8;
+    if (p.bmask)
+      hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, true, true>), dim3(grid), dim3(NW * 64), 0, s,
+                         (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, BH, p.H, p.N,
+                         p.causal, p.scale, p.scale * kLog2e, p.kv_len, p.bmask, nsplit, part);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, false, true>), dim3(grid), dim3(NW * 64), 0, s,
+                         (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, BH, p.H, p.N,
+                         p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr, nsplit, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t count = (size_t)BH * p.N * D;
+    e = launch_sum<T>(part, nsplit, count, p.scale, dK, s);
+    if (e != hipSuccess) return e;
+    return launch_sum<T>(part + (size_t)nsplit * count, nsplit, count, 1.0f, dV, s);
+  }
+  const int nlog = BH * TK;
   const int grid = (nlog + 7) / 8 * 8;
   if (p.bmask)
     hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal,
-                       p.scale, p.scale * kLog2e, p.kv_len, p.bmask);
+                       p.scale, p.scale * kLog2e, p.kv_len, p.bmask, 1, nullptr);
   else
     hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, false>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal,
-                       p.scale, p.scale * kLog2e, p.kv_len, nullptr);
+                       p.scale, p.scale * kLog2e, p.kv_len, nullptr, 1, nullptr);
   return hipGetLastError();
 }
 
 template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                              const void* O, const float* L, float* Dv, void* dQ, hipStream_t s) {
+                              const void* O, const float* L, float* Dv, void* dQ, hipStream_t s, int nsplit,
+                              float* part) {
   constexpr int QT = 32 * NW;
   const int TQ = (p.N + QT - 1) / QT;
-  const int nlog = p.B * p.H * TQ;
+  const int BH = p.B * p.H;
+  if (nsplit > 1) {
+    const int grid = (BH * TQ * nsplit + 7) / 8 * 8;
+    if (p.bmask)
+      hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, true, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                         (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, BH, p.H, p.N, p.causal,
+                         p.scale, p.scale * kLog2e, p.kv_len, p.bmask, nsplit, part);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, false, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
+                         (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, BH, p.H, p.N, p.causal,
+                         p.scale, p.scale * kLog2e, p.kv_len, nullptr, nsplit, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_sum<T>(part, nsplit, (size_t)BH * p.N * D, p.scale, dQ, s);
+  }
+  const int nlog = BH * TQ;
   const int grid = (nlog + 7) / 8 * 8;
   if (p.bmask)
     hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N,
-                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, p.bmask);
+                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, p.bmask, 1, nullptr);
   else
     hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, false>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N,
-                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr);
+                       p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr, 1, nullptr);
   return hipGetLastError();
 }
 
@@ -695,19 +823,68 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
 // Tile choices (measured on MI355X): for bf16 head dims up to 80, two 4-wave workgroups per CU with
 // 64-query stages (waves of different workgroups share a SIMD, so their MFMA and VALU phases
 // interleave).  At d = 128 the register file holds two waves per SIMD only with V in LDS: one
-// 8-wave workgroup per CU with 32-query stages for large grids, 4-wave workgroups otherwise.
+// 8-wave workgroup per CU with 32-query stages for large grids, 4-wave workgroups otherwise.  dQ:
+// 4-wave workgroups, two per CU; key tiles of 32 for head dims up to 80, 64 at d = 128.
+struct BwdTiles {
+  int kt;  // keys per dK/dV workgroup
+  int bq;  // query rows per dK/dV stage
+  int bk;  // key rows per dQ tile
+};
+static BwdTiles bwd_tiles(int dtype, const Problem& p) {
+  if (dtype == kF32) return {128, 32, 32};
+  if (p.d <= 80) return {128, 64, 32};
+  if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512) return {256, 32, 64};
+  return {128, 64, 64};
+}
+
+// Chunks per workgroup chain for the split backward, by the rule the forward uses: split only
+// grids with fewer than ~4 workgroups per CU whose chains are long (N >= 2048 in bfloat16, 256
+// in float32), into chunks of at least four tiles, at most kMaxSplits.
+static int chain_splits(int dtype, const Problem& p, long items, int chain_tiles) {
+  if (items >= 1024 || p.N < (dtype == kBF16 ? 2048 : 256)) return 1;
+  int s = (int)((1280 + items - 1) / items);
+  s = s > kMaxSplits ? kMaxSplits : s;
+  s = s > chain_tiles / 4 ? chain_tiles / 4 : s;
+  return s >= 2 ? s : 1;
+}
+static int dq_splits(int dtype, const Problem& p) {
+  const BwdTiles t = bwd_tiles(dtype, p);
+  return chain_splits(dtype, p, (long)p.B * p.H * ((p.N + 127) / 128), (p.N + t.bk - 1) / t.bk);
+}
+static int dkdv_splits(int dtype, const Problem& p) {
+  const BwdTiles t = bwd_tiles(dtype, p);
+  return chain_splits(dtype, p, (long)p.B * p.H * ((p.N + t.kt - 1) / t.kt), (p.N + t.bq - 1) / t.bq);
+}
+static size_t dq_workspace(int dtype, const Problem& p) {
+  const int sq = dq_splits(dtype, p);
+  return sq > 1 ? (size_t)sq * p.B * p.H * p.N * p.d * sizeof(float) : 0;
+}
+static size_t dkdv_workspace(int dtype, const Problem& p) {
+  const int sk = dkdv_splits(dtype, p);
+  return sk > 1 ? 2 * (size_t)sk * p.B * p.H * p.N * p.d * sizeof(float) : 0;
+}
+
+size_t bwd_workspace_bytes(int dtype, const Problem& p) {
+  const size_t a = dq_workspace(dtype, p), b = dkdv_workspace(dtype, p);
+  return a > b ? a : b;
+}
+
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                       const float* L, const float* Dv, void* dK, void* dV, hipStream_t s) {
+                       const float* L, const float* Dv, void* dK, void* dV, hipStream_t s, void* workspace,
+                       size_t workspace_bytes) {
+  const size_t need = dkdv_workspace(dtype, p);
+  const int ns = (need > 0 && workspace && workspace_bytes >= need) ? dkdv_splits(dtype, p) : 1;
+  float* part = (float*)workspace;
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
     if constexpr (DT == kF32) {                                                                     \
-      return launch_dkdv_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+      return launch_dkdv_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);            \
     } else if constexpr (DD <= 80) {                                                                \
-      return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+      return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);            \
     } else {                                                                                        \
-      if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512)                                             \
-        return launch_dkdv_t<T, DD, 8, 32, 1, true>(p, Q, K, V, dO, L, Dv, dK, dV, s);              \
-      return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s);                      \
+      if (bwd_tiles(dtype, p).kt == 256)                                                            \
+        return launch_dkdv_t<T, DD, 8, 32, 1, true>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);    \
+      return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);            \
     }                                                                                               \
   }
   ATTN_BWD_CASES(X)
@@ -715,14 +892,17 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
   return hipErrorInvalidValue;
 }
 
-// dQ: 4-wave workgroups, two per CU; key tiles of 32 for head dims up to 80, 64 at d = 128.
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                     const void* O, const float* L, float* Dv, void* dQ, hipStream_t s) {
+                     const void* O, const float* L, float* Dv, void* dQ, hipStream_t s, void* workspace,
+                     size_t workspace_bytes) {
+  const size_t need = dq_workspace(dtype, p);
+  const int ns = (need > 0 && workspace && workspace_bytes >= need) ? dq_splits(dtype, p) : 1;
+  float* part = (float*)workspace;
 #define X(T, DT, DD) \
   if (dtype == DT && p.d == DD) {                                                                  \
-    if constexpr (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s); \
-    else if constexpr (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s); \
-    else return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s);                      \
+    if constexpr (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part); \
+    else if constexpr (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part); \
+    else return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part);            \
   }
   ATTN_BWD_CASES(X)
 #undef X

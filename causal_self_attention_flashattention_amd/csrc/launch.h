@@ -33,14 +33,20 @@ size_t fwd_workspace_bytes(int dtype, const Problem& p);
 hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void* dO, float* Dv,
                          hipStream_t stream);
 
+// dK/dV and dQ.  With a workspace of at least bwd_workspace_bytes(dtype, p) bytes (non-zero only
+// for grids too small to fill the chip) each workgroup chain is split into chunks whose float32
+// partials a sum kernel adds in fixed order; the two calls may share one workspace (dQ's sum runs
+// before dK/dV's partials are written, on the same stream).
+size_t bwd_workspace_bytes(int dtype, const Problem& p);
 hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
                        const void* dO, const float* L, const float* Dv, void* dK, void* dV,
-                       hipStream_t stream);
+                       hipStream_t stream, void* workspace = nullptr, size_t workspace_bytes = 0);
 
 // dQ; with O != nullptr it also computes D = rowsum(O o dO) for its rows and stores it to Dv
 // (which is then an output), else it reads D from Dv.
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V,
-                     const void* dO, const void* O, const float* L, float* Dv, void* dQ, hipStream_t stream);
+                     const void* dO, const void* O, const float* L, float* Dv, void* dQ, hipStream_t stream,
+                     void* workspace = nullptr, size_t workspace_bytes = 0);
 
 // Small problems: the dQ and dK/dV work of attn_bwd in a single launch (both halves independent;
 // D stored by the dQ half).  bwd_small_applies tells when this path is used.

@@ -132,6 +132,21 @@ int attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void
                          void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
                          int dtype, const int32_t* kv_len, const uint8_t* block_mask, hipStream_t stream);
 
+/* Bytes of workspace attn_bwd_ex can use for this shape: non-zero when the dQ or dK/dV grid is
+ * too small to fill the chip, in which case each workgroup's chain (key tiles for dQ, query tiles
+ * for dK/dV) is split over several workgroups whose float32 partials a sum kernel adds up in a
+ * fixed order.  0 on bad arguments. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/* attn_bwd with every option: block_mask as for attn_bwd_blocksparse (NULL = none) and a
+ * caller-owned device workspace, used as for attn_fwd_ex (split path when workspace_bytes >=
+ * attn_bwd_workspace_bytes(...), the plain launches otherwise).  Deterministic either way; the
+ * split path agrees with attn_bwd to rounding. */
+int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                int dtype, const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
 /* How many kernels attn_bwd launches for this problem: 1 when the dQ and dK/dV work share one
  * launch (small bfloat16 problems with d <= 80, where the grid would otherwise leave CUs idle),
  * 2 otherwise (attn_bwd_dq with O, then attn_bwd_dkdv).  Negative attn_status on bad arguments. */

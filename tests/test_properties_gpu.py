@@ -114,7 +114,8 @@ def test_deterministic_and_substeps_equal_bwd(dtype, d):
     runs = []
     for _ in range(2):
         o, L = attn.fwd(x["q"], x["k"], x["v"], causal=True, kv_len=x["kv_len"])
-        runs.append((o, L) + attn.bwd(x["q"], x["k"], x["v"], o, x["do"], L, causal=True, kv_len=x["kv_len"]))
+        runs.append((o, L) + attn.bwd(x["q"], x["k"], x["v"], o, x["do"], L, causal=True, kv_len=x["kv_len"],
+                                      workspace=None))
     for t1, t2 in zip(*runs):
         assert torch.equal(t1, t2)
     o, L = runs[0][:2]

@@ -1,9 +1,12 @@
-"""Split-key forward (attn_fwd_ex with a workspace): for grids too small to fill the chip the key
-range of each query tile is cut into chunks on separate workgroups, and a second kernel merges the
-partial (max, sum, unnormalised O) triples with the online-softmax rescaling of the hand-out's
-Algorithm 1.  Both the split and the plain path are compared with the float64 oracle on shapes
-where the split is planned, including key padding, block-sparse masks with keyless rows, and
-sequences shorter than one chunk per split."""
+"""Split paths for grids too small to fill the chip (attn_fwd_ex / attn_bwd_ex with a workspace).
+
+Forward: the key range of each query tile is cut into chunks on separate workgroups, and a second
+kernel merges the partial (max, sum, unnormalised O) triples with the online-softmax rescaling of
+the hand-out's Algorithm 1.  Backward: the dQ kernel's key chain and the dK/dV kernel's query chain
+are cut the same way and float32 partials are summed in a fixed order.  Split and plain paths are
+compared with the float64 oracle on shapes where the split is planned, including key padding,
+block-sparse masks with keyless rows, and chains shorter than one chunk per split; the split
+backward is also checked to be deterministic."""
 
 import math
 
@@ -99,3 +102,51 @@ def test_large_grids_plan_no_split():
     assert attn.fwd_workspace_bytes(4, 20, 4096, 64, torch.bfloat16) == 0
     assert attn.fwd_workspace_bytes(1, 36, 16384, 128, torch.bfloat16) == 0
     assert attn.fwd_workspace_bytes(4, 32, 2048, 80, torch.bfloat16) == 0
+
+
+BWD_CASES = [
+    # B, H, N, d, dtype, causal, kv_len, block-mask density
+    (1, 1, 4096, 64, "bf16", True, None, None),
+    (1, 1, 2304, 128, "bf16", False, [2000], None),
+    (1, 2, 2100, 80, "bf16", True, None, 0.35),
+    (2, 1, 700, 32, "f32", True, [700, 512], None),
+    (1, 1, 1100, 128, "f32", False, None, None),
+    (1, 1, 513, 16, "f32", True, None, 0.5),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,kv,density", BWD_CASES)
+def test_split_backward_matches_oracle(B, H, N, d, dtype, causal, kv, density):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert attn.bwd_workspace_bytes(B, H, N, d, tdt) > 0, "the split backward should be planned here"
+    inp = make_inputs(B, H, N, d, dtype, seed=70 + N, kv_len=kv)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    kvd = None if inp["kv_len"] is None else inp["kv_len"].cuda()
+    bm = None
+    if density is not None:
+        tb = attn.mask_blocks(N)
+        bm = (np.random.default_rng(N).random((tb, tb)) < density).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+        bm[1, :] = 0
+    scale = 1.0 / math.sqrt(d)
+    o, L = attn.fwd(q, k, v, causal=causal, scale=scale, kv_len=kvd, block_mask=bm)
+    runs = [attn.bwd(q, k, v, o, do, L, causal=causal, scale=scale, kv_len=kvd, block_mask=bm) for _ in range(2)]
+    plain = attn.bwd(q, k, v, o, do, L, causal=causal, scale=scale, kv_len=kvd, block_mask=bm, workspace=None)
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.equal(a, b), "split backward not deterministic"
+    assert torch.equal(runs[0][3], plain[3]), "D must not depend on the split"
+    kw = dict(causal=causal, scale=scale, kv_len=kv, block_mask=bm, block=64)
+    rq, rk, rv, _ = ref.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], **kw)
+    for tag, (dq, dk, dv, _) in (("split", runs[0]), ("plain", plain)):
+        for b in range(B):
+            for h in range(H):
+                _close(f"dQ {tag} (b={b}, h={h})", dq[b, h], rq[b, h], dtype)
+                _close(f"dK {tag} (b={b}, h={h})", dk[b, h], rk[b, h], dtype)
+                _close(f"dV {tag} (b={b}, h={h})", dv[b, h], rv[b, h], dtype)
+
+
+def test_backward_plans_no_split_for_large_grids():
+    assert attn.bwd_workspace_bytes(4, 20, 4096, 64, torch.bfloat16) == 0
+    assert attn.bwd_workspace_bytes(1, 36, 16384, 128, torch.bfloat16) == 0
+    assert attn.bwd_workspace_bytes(4, 12, 512, 64, torch.bfloat16) == 0
