@@ -8,6 +8,7 @@ not built, or no GPU is present, these functions raise.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 
@@ -133,6 +134,7 @@ def block_mask_tensor(block_mask, N, device):
     return (m != 0).to(device=device, dtype=torch.uint8).contiguous()
 
 
+@functools.lru_cache(maxsize=1024)
 def fwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
     """Workspace attn_fwd_ex can use for this shape (0 when the plain single launch is best)."""
     return int(load_library().attn_fwd_workspace_bytes(B, H, N, d, _DTYPES[dtype]))
@@ -164,6 +166,7 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, kv_len=None, o
     return o, L
 
 
+@functools.lru_cache(maxsize=1024)
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
     """Workspace attn_bwd_ex can use for this shape (0 when the plain launches are best)."""
     return int(load_library().attn_bwd_workspace_bytes(B, H, N, d, _DTYPES[dtype]))
