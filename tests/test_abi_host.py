@@ -137,3 +137,60 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         bnd.fwd(q, q, q)
+
+
+def _fwd_ex(lib, **kw):
+    p = dict(Q=A, K=A + SZ, V=A + 2 * SZ, O=A + 3 * SZ, L=A + 4 * SZ, B=1, H=1, N=4096, d=64, causal=1, scale=0.125,
+             dtype=1, kv=None, mask=None, ws=A + 5 * SZ, wsb=1 << 26)
+    p.update(kw)
+    return lib.attn_fwd_ex(p["Q"], p["K"], p["V"], p["O"], p["L"], p["B"], p["H"], p["N"], p["d"], p["causal"],
+                           p["scale"], p["dtype"], p["kv"], p["mask"], p["ws"], p["wsb"], None)
+
+
+def _bwd_ex(lib, **kw):
+    p = dict(Q=A, K=A + SZ, V=A + 2 * SZ, O=A + 3 * SZ, dO=A + 4 * SZ, L=A + 5 * SZ, dQ=A + 6 * SZ,
+             dK=A + 7 * SZ, dV=A + 8 * SZ, D=A + 9 * SZ, B=1, H=1, N=4096, d=64, causal=1, scale=0.125, dtype=1,
+             kv=None, mask=None, ws=A + 10 * SZ, wsb=1 << 26)
+    p.update(kw)
+    return lib.attn_bwd_ex(p["Q"], p["K"], p["V"], p["O"], p["dO"], p["L"], p["dQ"], p["dK"], p["dV"], p["D"], p["B"],
+                           p["H"], p["N"], p["d"], p["causal"], p["scale"], p["dtype"], p["kv"], p["mask"], p["ws"],
+                           p["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=A + 5 * SZ + 8), E_ALIGN),            # misaligned workspace
+    (dict(ws=A + 3 * SZ + 4096), E_ALIAS),         # workspace inside O
+    (dict(ws=A + 2 * SZ), E_ALIAS),                # workspace == V (an input)
+    (dict(mask=A + 4 * SZ + 64), E_ALIAS),         # mask inside L (an output)
+    (dict(N=65600, mask=A + 6 * SZ), E_SHAPE),     # block-sparse needs N <= 65536
+    (dict(Q=None), E_NULL), (dict(d=48), E_HEADDIM),
+])
+def test_fwd_ex_rejects_bad_arguments(lib, kw, status):
+    assert _fwd_ex(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=A + 10 * SZ + 4), E_ALIGN),
+    (dict(ws=A + 6 * SZ), E_ALIAS),                # workspace == dQ
+    (dict(ws=A + 3 * SZ + 256), E_ALIAS),          # workspace inside O (an input)
+    (dict(mask=A + 8 * SZ), E_ALIAS),              # mask == dV
+    (dict(N=70000, mask=A + 11 * SZ), E_SHAPE),
+    (dict(D=None), E_NULL), (dict(dtype=3), E_DTYPE),
+])
+def test_bwd_ex_rejects_bad_arguments(lib, kw, status):
+    assert _bwd_ex(lib, **kw) == status
+
+
+def test_workspace_queries(lib):
+    # host-only planning: small grids with long chains get a workspace, large grids none, bad args 0
+    assert lib.attn_fwd_workspace_bytes(1, 1, 4096, 64, 1) > 0
+    assert lib.attn_fwd_workspace_bytes(1, 1, 300, 64, 0) > 0           # float32 splits shorter chains
+    assert lib.attn_fwd_workspace_bytes(1, 1, 1000, 64, 1) == 0         # bfloat16 chain too short
+    assert lib.attn_fwd_workspace_bytes(4, 20, 4096, 64, 1) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 1, 4096, 48, 1) == 0         # unsupported head dim
+    assert lib.attn_bwd_workspace_bytes(1, 1, 4096, 128, 1) > 0
+    assert lib.attn_bwd_workspace_bytes(1, 36, 16384, 128, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(0, 1, 4096, 64, 1) == 0
+    # the workspace scales with the planned chunks, never beyond 16 partial copies of the output
+    w = lib.attn_fwd_workspace_bytes(1, 1, 16384, 128, 1)
+    assert 0 < w <= 16 * 16384 * (128 + 2) * 4
