@@ -833,7 +833,7 @@ struct BwdTiles {
 static BwdTiles bwd_tiles(int dtype, const Problem& p) {
   if (dtype == kF32) return {128, 32, 32};
   if (p.d <= 80) return {128, 64, 32};
-  if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512) return {256, 32, 64};
+  if ((long)p.B * p.H * ((p.N + 255) / 256) >= 512) return {256, 64, 64};
   return {128, 64, 64};
 }
 
@@ -883,7 +883,7 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
       return launch_dkdv_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);            \
     } else {                                                                                        \
       if (bwd_tiles(dtype, p).kt == 256)                                                            \
-        return launch_dkdv_t<T, DD, 8, 32, 1, true>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);    \
+        return launch_dkdv_t<T, DD, 8, 64, 1, true>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);    \
       return launch_dkdv_t<T, DD, 4, 64, 1>(p, Q, K, V, dO, L, Dv, dK, dV, s, ns, part);            \
     }                                                                                               \
   }
