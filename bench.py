@@ -5,8 +5,10 @@ One step = the whole path over one batch: attn_fwd, then the backward exactly as
 -- either its two kernels called one by one (attn_bwd_dq, which also computes D = rowsum(O o dO),
 then attn_bwd_dkdv) or, for small problems, attn_bwd itself, whose dQ and dK/dV work share one
 launch -- on torch's current HIP stream, with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
-bracketed by torch.cuda.synchronize(); HIP events recorded on the same stream between the kernels
-give each kernel's average duration.  Prints one JSON line.
+bracketed by torch.cuda.synchronize(); on every --event-every-th timed step, HIP events recorded on
+the same stream between the kernels give each kernel's average duration (an event record between
+two kernels leaves a gap of a few microseconds, which on the small workload would add about a
+quarter to every step if each step carried them).  Prints one JSON line.
 
 Algorithmic FLOPs (matrix products only, 2 FLOPs per multiply-add; causal-skipped half and the
 dQ kernel's recompute of S and dP not counted):
@@ -140,6 +142,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record the per-kernel HIP events on every n-th timed step (1 = every step)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the attention step, time a plain device-to-device copy of this many bytes "
                          "(the reference kernel that HBM byte counters are scaled against)")
@@ -222,7 +226,9 @@ def main():
     for _ in range(args.warmup - max(1, args.warmup // 2)):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    n_ev = (args.steps + every - 1) // every
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(n_ev)]
     for e in evs:  # materialise the events before the timed region
         for x in e:
             x.record()
@@ -230,13 +236,13 @@ def main():
     hev = [[ctypes.c_void_p(x.cuda_event) for x in e] for e in evs]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(hev[i])
+        step(hev[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    per_kernel_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+    per_kernel_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n_ev
                      for j, name in enumerate(KERNELS)}
-    event_ms_per_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+    event_ms_per_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / n_ev
 
     work = kernel_work(w, kv)
     P = npairs(w.N, kv, w.causal)
@@ -279,7 +285,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "kv_len": kv, "seed": w.seed if args.seed is None else args.seed,
                    "pct_of_peak": 100.0 * value / peak, "peak_tflops": peak,
-                   "event_ms_per_step": event_ms_per_step, "kernels": kernels},
+                   "event_ms_per_step": event_ms_per_step, "event_steps": n_ev, "kernels": kernels},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
