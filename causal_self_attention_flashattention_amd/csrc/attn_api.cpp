@@ -34,7 +34,9 @@ int check_common(int B, int H, int N, int d, int dtype, float scale, bool need_s
   const int64_t elems = (int64_t)B * H * N * d;
   if (elems >= ((int64_t)1 << 31)) return ATTN_E_SHAPE;
   if (!attn::fwd_supported(dtype, d)) return ATTN_E_HEADDIM;
-  if (need_scale && !std::isfinite(scale)) return ATTN_E_SCALE;
+  // The kernels take row maxima of the unscaled scores and mask before scaling, both of which
+  // assume scale > 0.
+  if (need_scale && !(std::isfinite(scale) && scale > 0.f)) return ATTN_E_SCALE;
   return ATTN_OK;
 }
 
@@ -77,7 +79,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_E_ALIAS: return "an output buffer overlaps an input or another output";
     case ATTN_E_LAUNCH: return "kernel launch failed";
-    case ATTN_E_SCALE: return "scale is not finite";
+    case ATTN_E_SCALE: return "scale is not a finite number greater than 0";
     default: return "unknown status";
   }
 }

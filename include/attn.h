@@ -48,7 +48,7 @@ typedef enum {
   ATTN_E_ALIGN = -5,   /* a pointer is not 16-byte aligned */
   ATTN_E_ALIAS = -6,   /* an output buffer overlaps an input or another output */
   ATTN_E_LAUNCH = -7,  /* a kernel launch failed (HIP error) */
-  ATTN_E_SCALE = -8    /* scale is not a finite number */
+  ATTN_E_SCALE = -8    /* scale is not a finite number > 0 */
 } attn_status;
 
 /* Forward pass (Algorithm 1 of the handout, §4.1, with the causal flag of Problem
@@ -57,7 +57,7 @@ typedef enum {
  *   O        out: [B,H,N,d] dtype, softmax(mask(scale Q K^T)) V
  *   L        out: [B,H,N] float32, natural-log logsumexp of the scaled, masked scores
  *   causal      : 0 or non-zero
- *   scale       : softmax scale, normally 1/sqrt(d)
+ *   scale       : softmax scale, finite and > 0; normally 1/sqrt(d)
  *   kv_len      : device int32[B], 1 <= kv_len[b] <= N (values outside are clamped), or NULL
  * O and L must not overlap any input or each other. */
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,

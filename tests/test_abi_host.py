@@ -84,6 +84,7 @@ def _bwd(lib, **kw):
     (dict(B=1024, H=1024, N=1024, d=64), E_SHAPE),
     (dict(d=96), E_HEADDIM), (dict(d=48), E_HEADDIM), (dict(dtype=7), E_DTYPE),
     (dict(scale=float("nan")), E_SCALE), (dict(scale=float("inf")), E_SCALE),
+    (dict(scale=0.0), E_SCALE), (dict(scale=-0.125), E_SCALE),
     (dict(Q=A + 8), E_ALIGN), (dict(L=A + 4 * SZ + 4), E_ALIGN),
     (dict(O=A + 2 * SZ + 16), E_ALIAS),   # O overlaps V
     (dict(L=A + 3 * SZ + 64), E_ALIAS),   # L inside O
@@ -100,7 +101,7 @@ def test_fwd_rejects_bad_arguments(lib, kw, status):
     (dict(dQ=A), E_ALIAS),                # dQ == Q
     (dict(dK=A + 6 * SZ), E_ALIAS),       # dK == dQ
     (dict(D=A + 5 * SZ), E_ALIAS),        # D == L
-    (dict(scale=float("-inf")), E_SCALE),
+    (dict(scale=float("-inf")), E_SCALE), (dict(scale=0.0), E_SCALE), (dict(scale=-1.0), E_SCALE),
 ])
 def test_bwd_rejects_bad_arguments(lib, kw, status):
     assert _bwd(lib, **kw) == status
