@@ -823,7 +823,7 @@ hipError_t launch_rowdot(int dtype, const Problem& p, const void* O, const void*
 // Tile choices (measured on MI355X): for bf16 head dims up to 80, two 4-wave workgroups per CU with
 // 64-query stages (waves of different workgroups share a SIMD, so their MFMA and VALU phases
 // interleave).  At d = 128 the register file holds two waves per SIMD only with V in LDS: one
-// 8-wave workgroup per CU with 32-query stages for large grids, 4-wave workgroups otherwise.  dQ:
+// 8-wave workgroup per CU with 64-query stages for large grids, 4-wave workgroups otherwise.  dQ:
 // 4-wave workgroups, two per CU; key tiles of 32 for head dims up to 80, 64 at d = 128.
 struct BwdTiles {
   int kt;  // keys per dK/dV workgroup

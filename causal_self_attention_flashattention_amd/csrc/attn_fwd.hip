@@ -28,8 +28,14 @@ constexpr float kRescaleSlack = 8.0f;
 // a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
 // (layout: [nsplit][BH*N][D] floats, then [nsplit][BH*N][2] floats) instead of O and L, and
 // fwd_combine_kernel merges the chunks with Algorithm 1's rescaling.
-template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+//
+// With G = 2 the workgroup has two groups of NW waves over the same queries, and key tiles of
+// 2 BK keys: group g takes keys [g BK, (g + 1) BK) of every tile, so each wave's chain of tiles is
+// half as long (for grids too small to fill the chip, where that chain sets the time).  The two
+// groups' (running max, row sum, unnormalised O) are merged through LDS at the end, with the same
+// rescaling as between tiles.
+template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false, int G = 1>
+__global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                            const T* __restrict__ V, T* __restrict__ O,
                                                            float* __restrict__ Lse, int BH, int H, int N,
                                                            int causal, float scale_log2,
@@ -37,18 +43,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
                                                            const uint8_t* __restrict__ bmask, int nsplit,
                                                            float* __restrict__ part) {
   using M = Mfma<T>;
-  constexpr int NT = NW * 64;
+  constexpr int NT = G * NW * 64;         // threads of the workgroup
   constexpr int QT = 32 * NW;             // queries per workgroup
   constexpr int DP = (D + 31) / 32 * 32;  // head dim rounded up to a 32-row MFMA block
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
-  constexpr int NB = BK / 32;
+  constexpr int NB = BK / 32;             // key blocks per wave and tile
+  constexpr int BKT = G * BK;             // keys per tile
   constexpr int LD = lds_pitch<T, DP>();  // LDS row stride (elements)
-  constexpr int TILE = BK * LD * (int)sizeof(T);  // bytes of one K or V tile
+  constexpr int TILE = BKT * LD * (int)sizeof(T);  // bytes of one K or V tile
   constexpr int SHIFT = BK == 64 ? 0 : 1;          // key tiles per mask block = 1 << SHIFT
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
+  static_assert(G == 1 || (G == 2 && BK == 64 && !BSP && !SPLIT), "two key groups: dense, unsplit, BK = 64");
 
   // Two stages of (K tile, V tile): the next tile is written while the current one is read; then,
   // for block-sparse calls, one byte per mask column (which of this workgroup's rows see it).
@@ -71,7 +79,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   O += base;
   Lse += (size_t)bh * N;
 
-  const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
+  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int q0 = qt * QT;
   const int qw = q0 + 32 * w;  // first query of this wave
   const int q = qw + col;      // this lane's query
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
-  const int nkt = (kend + BK - 1) / BK;
+  const int nkt = (kend + BKT - 1) / BKT;
   // This workgroup's key tiles [t_lo, t_hi): all of them, or one of nsplit equal chunks.
   const int chunk = (nkt + nsp - 1) / nsp;
   const int t_lo = SPLIT ? min(nkt, split * chunk) : 0;
@@ -105,8 +114,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
   float m_run = -INFINITY, l_part = 0.f;
 
   if constexpr (DP > D) {
-    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + TILE);
-    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 3 * TILE);
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + TILE);
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 3 * TILE);
   }
   // Key tiles in loop order: all of [0, nkt), or (block-sparse) those some row of this workgroup
   // may see; the current, next and next-but-one tiles are tracked for the two-stage pipeline.
@@ -117,25 +126,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
     cur = next_live_tile(map, t_lo, t_hi, SHIFT);
   }
   auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
-  TileCopy<T, BK, D, LD, NT> kc, vc;
+  TileCopy<T, BKT, D, LD, NT> kc, vc;
   if (cur < t_hi) {
-    kc.load(rk, cur * BK);
-    vc.load(rv, cur * BK);
+    kc.load(rk, cur * BKT);
+    vc.load(rv, cur * BKT);
     kc.store(lds);
     vc.store(lds + TILE);
   }
   __syncthreads();
   int nxt = cur < t_hi ? after(cur) : t_hi;
   if (nxt < t_hi) {
-    kc.load(rk, nxt * BK);
-    vc.load(rv, nxt * BK);
+    kc.load(rk, nxt * BKT);
+    vc.load(rv, nxt * BKT);
   }
 
   for (int it = 0; cur < t_hi; ++it) {
-    const lds_t* ktile = lds + (it & 1) * 2 * TILE;
+    // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
+    const lds_t* ktile = lds + (it & 1) * 2 * TILE + grp * BK * LD * (int)sizeof(T);
     const lds_t* vtile = ktile + TILE;
-    const int k0 = cur * BK;
-    bool run = wave_live && !(causal && k0 > qw_last);
+    const int k0 = cur * BKT + grp * BK;
+    // (k0 is a multiple of 64 and qw of 32, so a wave that runs has key k0 visible in every row.)
+    bool run = wave_live && k0 < kend && !(causal && k0 > qw_last);
     if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
     if (run) {
       f32x16 s[NB];
@@ -196,13 +207,41 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(const T* __restrict__
     }
     __syncthreads();
     if (nxt2 < t_hi) {
-      kc.load(rk, nxt2 * BK);
-      vc.load(rv, nxt2 * BK);
+      kc.load(rk, nxt2 * BKT);
+      vc.load(rv, nxt2 * BKT);
     }
     cur = nxt;
     nxt = nxt2;
   }
 
+  if constexpr (G == 2) {
+    // Group 1 hands (m, l, O) to the wave of group 0 that owns the same queries; the tiles are no
+    // longer read (the loop ended on a barrier and staged nothing after it).
+    constexpr int F = 2 + 16 * NDB;  // floats per lane
+    static_assert(NW * 64 * F * 4 <= 4 * TILE, "merge buffer fits in the tile stages");
+    float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
+    if (grp == 1) {
+      mrg[0] = m_run;
+      mrg[64] = l_part;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mrg[(2 + 16 * i + e) * 64] = o[i][e];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = mrg[0], l1 = mrg[64];
+    const float m = fmaxf(m_run, m1);
+    // A group that saw no key of this row has m = -inf and contributes nothing.
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[i][e] = o[i][e] * a0 + mrg[(2 + 16 * i + e) * 64] * a1;
+    l_part = l_part * a0 + l1 * a1;
+    m_run = m;
+  }
   const float l_tot = l_part + swap_halves(l_part);
   if constexpr (SPLIT) {
     // Unnormalised partial: sum_j exp2(s_j - m) v_j, with m and sum_j exp2(s_j - m) beside it.
@@ -301,6 +340,15 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
   if (c == 0) Lse[row] = lsum > 0.f ? (m + fast_log2(lsum)) * kLn2 : -INFINITY;
 }
 
+// Two key groups per workgroup (fwd_kernel's G = 2) when the grid of 128-query workgroups is at
+// most one per CU and the longest key chain has at least four 64-key tiles: each CU then runs
+// one workgroup, whose chain the second group halves.  Measured on MI355X: B=4 H=12 N=512 d=64
+// 11.1 -> 10.5 us, B=2 H=16 N=1024 d=64 18.1 -> 16.1 us (64-query workgroups with two groups,
+// two per CU, were slower than these).
+static bool fwd_two_groups(const Problem& p, long items) {
+  return items <= 256 && p.N >= 256;
+}
+
 template <typename T, int D, int NW, int BK, int OCC>
 static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O,
                                float* L, hipStream_t stream, int nsplit = 1, float* part = nullptr) {
@@ -327,6 +375,14 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
     return hipGetLastError();
   }
   const int grid = (BH * TQ + 7) / 8 * 8;
+  if constexpr (sizeof(T) == 2 && BK == 64) {
+    if (!p.bmask && fwd_two_groups(p, BH * TQ)) {
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, 1, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, stream,
+                         (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
+                         nullptr, 1, nullptr);
+      return hipGetLastError();
+    }
+  }
   if (p.bmask)
     hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, stream, (const T*)Q,
                        (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len, p.bmask, 1,

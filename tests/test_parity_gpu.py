@@ -33,6 +33,14 @@ SMALL += [
     ("bf16", 1, 3, 384, 64, True, [300]),
     ("bf16", 1, 2, 130, 128, False, None),
     ("f32", 1, 2, 96, 64, False, [50]),
+    # forward with two key groups per workgroup (grids of at most 256 query tiles, N >= 256) and
+    # either side of that threshold
+    ("bf16", 2, 3, 700, 128, True, [650, 700]),
+    ("bf16", 1, 2, 520, 80, True, [400]),
+    ("bf16", 1, 2, 333, 32, True, None),
+    ("bf16", 1, 2, 300, 16, False, [70]),
+    ("bf16", 1, 64, 512, 64, True, None),
+    ("bf16", 1, 65, 512, 64, True, None),
 ]
 
 
