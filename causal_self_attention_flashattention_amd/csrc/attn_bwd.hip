@@ -57,11 +57,11 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 // LDS bytes of the dK/dV body: two stages of (Q tile, dO tile, L row, D row), then either (DSELF)
 // one float of D per query row for rows up to kDselfMaxN, or (VLDS) the workgroup's V rows.
 constexpr int kDselfMaxN = 4096;
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false>
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, int G = 1>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
-  constexpr int TILE = BQ * lds_pitch<T, DP>() * (int)sizeof(T);
-  return 2 * (2 * TILE + 2 * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
+  constexpr int TILE = G * BQ * lds_pitch<T, DP>() * (int)sizeof(T);
+  return 2 * (2 * TILE + 2 * G * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
          (VLDS ? 32 * KB * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0) + (BSP ? kMaxMaskBlocks : 0);
 }
 
@@ -69,12 +69,17 @@ constexpr int dkdv_lds_bytes() {
 // does not read D: it first computes D = rowsum(O o dO) for every query row it will visit, in the
 // same fragment order as the D pre-pass, into LDS (requires N <= kDselfMaxN).  With VLDS the
 // workgroup's V rows are kept in LDS and read per block instead of being held in registers (frees
-// 32 VGPRs per key block at d = 128, where the register file is otherwise too small).  With BSP
+// 32 VGPRs per key block at d = 128, where the register file is otherwise too small).  With G = 2
+// the workgroup has two groups of NW waves over the same keys and stages of 2 BQ query rows: group
+// g takes rows [g BQ, (g + 1) BQ) of every stage, so each wave's chain of stages is half as long
+// (for grids too small to fill the chip); group 1's dK, dV are added to group 0's through LDS at
+// the end.  With BSP
 // the query tiles whose mask row meets none of the workgroup's key blocks are skipped, and each
 // wave skips the tiles its own mask block excludes.  With SPLIT the query tiles of every key tile
 // are cut into `nsplit` chunks, one workgroup each, which write unscaled float32 partial dK and dV
 // rows to `part` ([nsplit][BH*N][D] for dK, then the same for dV) for bwd_sum_kernel to add up.
-template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, bool SPLIT = false>
+template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, bool SPLIT = false,
+          int G = 1>
 __device__ __forceinline__ void dkdv_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
@@ -82,23 +87,25 @@ __device__ __forceinline__ void dkdv_body(
     float scale, float scale_log2, const int32_t* __restrict__ kv_len, const uint8_t* __restrict__ bmask,
     int nsplit = 1, float* __restrict__ part = nullptr) {
   using M = Mfma<T>;
-  constexpr int NT = NW * 64;
+  constexpr int NT = G * NW * 64;  // threads of the workgroup
   constexpr int KW = 32 * KB;  // keys per wave
   constexpr int KT = KW * NW;  // keys per workgroup
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
-  constexpr int NQB = BQ / 32;
+  constexpr int NQB = BQ / 32;   // query blocks per wave and stage
+  constexpr int BQS = G * BQ;    // query rows per stage
   constexpr int LD = lds_pitch<T, DP>();
-  constexpr int TILE = BQ * LD * (int)sizeof(T);
-  constexpr int STAGE = 2 * TILE + 2 * BQ * (int)sizeof(float);  // Q tile, dO tile, L row, D row
-  constexpr int SHIFT = BQ == 64 ? 0 : 1;                        // query tiles per mask block = 1 << SHIFT
-  static_assert(2 * BQ <= NT, "one thread per staged L / D value");
+  constexpr int TILE = BQS * LD * (int)sizeof(T);
+  constexpr int STAGE = 2 * TILE + 2 * BQS * (int)sizeof(float);  // Q tile, dO tile, L row, D row
+  constexpr int SHIFT = BQ == 64 ? 0 : 1;                         // query tiles per mask block = 1 << SHIFT
+  static_assert(2 * BQS <= NT, "one thread per staged L / D value");
+  static_assert(G == 1 || (G == 2 && !BSP && !SPLIT), "two query groups: dense and unsplit only");
   static_assert(!BSP || ((BQ == 32 || BQ == 64) && KT % kMaskBlock == 0 && KT / kMaskBlock <= 8),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
 
   lds_t* lds = (lds_t*)smem;
-  lds_t* map = lds + dkdv_lds_bytes<T, D, NW, BQ, DSELF, VLDS, KB, false>();
+  lds_t* map = lds + dkdv_lds_bytes<T, D, NW, BQ, DSELF, VLDS, KB, false, G>();
 
   const int TK = (N + KT - 1) / KT;
   const int nsp = SPLIT ? nsplit : 1;
@@ -114,7 +121,8 @@ __device__ __forceinline__ void dkdv_body(
   const size_t base = (size_t)bh * N * D;
   dK += base; dV += base;
 
-  const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = (int)(threadIdx.x >> 6) / NW;  // query group (G = 2) or 0
+  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int k0 = kt * KT;
   const int kw = k0 + KW * w;  // first key of this wave
   const bool wave_live = kw < kv;
@@ -155,17 +163,17 @@ __device__ __forceinline__ void dkdv_body(
         settle(kf[kb][ks]);
         if constexpr (!VLDS) settle(vf[kb][ks]);
       }
-    const int TQ = (N + BQ - 1) / BQ;
-    const int qt0 = causal ? k0 / BQ : 0;
+    const int TQ = (N + BQS - 1) / BQS;
+    const int qt0 = causal ? k0 / BQS : 0;
     // This workgroup's query tiles [qt_lo, qt_hi): all from qt0, or one of nsplit equal chunks.
     const int qchunk = (TQ - qt0 + nsp - 1) / nsp;
     const int qt_lo = SPLIT ? min(TQ, qt0 + split * qchunk) : qt0;
     const int qt_hi = SPLIT ? min(TQ, qt_lo + qchunk) : TQ;
 
-    // DSELF: D for rows [qt0*BQ, N), one row per thread at a time, kept in LDS after the stages.
+    // DSELF: D for rows [qt0*BQS, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
     if constexpr (DSELF) {
-      for (int r = qt0 * BQ + threadIdx.x; r < N; r += NT) {
+      for (int r = qt0 * BQS + threadIdx.x; r < N; r += NT) {
         const T* orow = Oin + base + (size_t)r * D;
         const T* grow = dO + base + (size_t)r * D;
         float part[2];
@@ -180,34 +188,35 @@ __device__ __forceinline__ void dkdv_body(
             part[h] = frag_dot(a, g, part[h]);
           }
         }
-        dself[r - qt0 * BQ] = -(part[0] + part[1]);
+        dself[r - qt0 * BQS] = -(part[0] + part[1]);
       }
     }
 
     if constexpr (DP > D) {
-      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds);
-      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + TILE);
-      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + STAGE);
-      zero_pad_cols<T, BQ, D, LD, DP, NT>(lds + STAGE + TILE);
+      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds);
+      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + TILE);
+      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + STAGE);
+      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + STAGE + TILE);
     }
-    TileCopy<T, BQ, D, LD, NT> qc, oc;
-    // One staged value per thread: L (threads < BQ) or D (threads BQ..2BQ-1).  L is scaled to
+    TileCopy<T, BQS, D, LD, NT> qc, oc;
+    // One staged value per thread: L (threads < BQS) or D (threads BQS..2BQS-1).  L is scaled to
     // log2 units and D negated only when written to LDS, so that no arithmetic waits on the load
     // here.  -D is the initial value of the dP accumulator, which then yields dP - D directly.
     float lrd = 0.f;
     auto load_stage = [&](int qt) {
-      qc.load(rq, qt * BQ);
-      oc.load(ro, qt * BQ);
+      qc.load(rq, qt * BQS);
+      oc.load(ro, qt * BQS);
       const int t = threadIdx.x;
-      if (t < (DSELF ? BQ : 2 * BQ))
-        lrd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t < BQ ? rl : rd, (qt * BQ + (t % BQ)) * 4, 0, 0));
+      if (t < (DSELF ? BQS : 2 * BQS))
+        lrd = __builtin_bit_cast(float,
+                                 __builtin_amdgcn_raw_buffer_load_b32(t < BQS ? rl : rd, (qt * BQS + (t % BQS)) * 4, 0, 0));
     };
     auto store_stage = [&](lds_t* st) {
       qc.store(st);
       oc.store(st + TILE);
-      if (threadIdx.x < (DSELF ? BQ : 2 * BQ))
+      if (threadIdx.x < (DSELF ? BQS : 2 * BQS))
         reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
-            threadIdx.x < BQ ? lrd * kLog2e : -lrd;
+            threadIdx.x < BQS ? lrd * kLog2e : -lrd;
     };
     // Query tiles in loop order: all of [qt0, TQ), or (block-sparse) those whose mask row meets one
     // of this workgroup's key blocks; current, next and next-but-one are tracked for the pipeline.
@@ -227,17 +236,18 @@ __device__ __forceinline__ void dkdv_body(
     if (nxt < qt_hi) load_stage(nxt);
 
     for (int it = 0; cur < qt_hi; ++it) {
-      const int q0 = cur * BQ;
+      const int q0 = cur * BQS;
       const lds_t* qtile = lds + (it & 1) * STAGE;
       const lds_t* otile = qtile + TILE;
       const __attribute__((address_space(3))) float* lrow =
           reinterpret_cast<const __attribute__((address_space(3))) float*>(qtile + 2 * TILE);
-      const __attribute__((address_space(3))) float* drow = DSELF ? dself + (cur - qt0) * BQ : lrow + BQ;
+      const __attribute__((address_space(3))) float* drow = DSELF ? dself + (cur - qt0) * BQS : lrow + BQS;
       bool run = wave_live;
       if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
       if (run) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
+        for (int qbw = 0; qbw < NQB; ++qbw) {
+          const int qb = grp * NQB + qbw;  // query block within the stage
           const int qb0 = q0 + qb * 32;
           if (qb0 >= N || (causal && qb0 + 31 < kw)) continue;  // past the end, or before this wave's keys
           // dP accumulators start at -D of their rows (accumulator row order), so after the products
@@ -326,6 +336,36 @@ __device__ __forceinline__ void dkdv_body(
     }
   }
 
+  if constexpr (G == 2) {
+    // Group 1 hands its dK, dV sums to the wave of group 0 that owns the same keys (every wave of
+    // the workgroup gets here; the stages are no longer read once the loop's last barrier passed).
+    constexpr int F = 2 * KB * NDB * 16;  // floats per lane
+    static_assert(NW * 64 * F * 4 <= 2 * STAGE, "merge buffer fits in the stages");
+    float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
+    if (grp == 1) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            mrg[((kb * NDB + i) * 32 + e) * 64] = dk[kb][i][e];
+            mrg[((kb * NDB + i) * 32 + 16 + e) * 64] = dv[kb][i][e];
+          }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          dk[kb][i][e] += mrg[((kb * NDB + i) * 32 + e) * 64];
+          dv[kb][i][e] += mrg[((kb * NDB + i) * 32 + 16 + e) * 64];
+        }
+  }
+
   if constexpr (SPLIT) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -391,15 +431,16 @@ __device__ __forceinline__ void dkdv_body(
   }
 }
 
-template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB, bool BSP, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(
+template <typename T, int D, int NW, int BQ, int OCC, bool VLDS, int KB, bool BSP, bool SPLIT = false, int G = 1>
+__global__ __launch_bounds__(G * NW * 64, OCC) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ Lse, const float* __restrict__ Dv, T* __restrict__ dK, T* __restrict__ dV,
     int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
     const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB, BSP>()];
-  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP, SPLIT>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV, BH,
-                                                       H, N, causal, scale, scale_log2, kv_len, bmask, nsplit, part);
+  __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB, BSP, G>()];
+  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP, SPLIT, G>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV,
+                                                          BH, H, N, causal, scale, scale_log2, kv_len, bmask, nsplit,
+                                                          part);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -411,7 +452,10 @@ constexpr int dq_lds_bytes() {
   return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T) + (BSP ? kMaxMaskBlocks : 0);
 }
 
-template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false>
+// With G = 2 the workgroup has two groups of NW waves over the same queries and key tiles of 2 BK
+// keys: group g takes keys [g BK, (g + 1) BK) of every tile, halving each wave's chain; group 1's
+// dQ sums are added to group 0's through LDS at the end (as in the forward and dK/dV bodies).
+template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false, int G = 1>
 __device__ __forceinline__ void dq_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
@@ -422,17 +466,19 @@ __device__ __forceinline__ void dq_body(
   // row belongs to exactly one workgroup) and stores it to Dv for the dK/dV kernel that follows;
   // otherwise it reads D from Dv.
   using M = Mfma<T>;
-  constexpr int NT = NW * 64;
+  constexpr int NT = G * NW * 64;  // threads of the workgroup
   constexpr int QT = 32 * NW;
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int NDB = DP / 32;
   constexpr int KS = D / M::KSTEP;
-  constexpr int NB = BK / 32;
+  constexpr int NB = BK / 32;      // key blocks per wave and tile
+  constexpr int BKT = G * BK;      // keys per tile
   constexpr int LD = lds_pitch<T, DP>();
-  constexpr int TILE = BK * LD * (int)sizeof(T);
+  constexpr int TILE = BKT * LD * (int)sizeof(T);
   constexpr int SHIFT = BK == 64 ? 0 : 1;  // key tiles per mask block = 1 << SHIFT
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
+  static_assert(G == 1 || (G == 2 && !BSP && !SPLIT), "two key groups: dense and unsplit only");
 
   lds_t* lds = (lds_t*)smem;
   lds_t* map = lds + 4 * TILE;
@@ -451,7 +497,8 @@ __device__ __forceinline__ void dq_body(
   const size_t base = (size_t)bh * N * D;
   dQ += base;
 
-  const int w = threadIdx.x >> 6, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
+  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int q0 = qt * QT;
   const int qw = q0 + 32 * w;
   const int q = qw + col;
@@ -462,7 +509,7 @@ __device__ __forceinline__ void dq_body(
 
   int kend = kv;
   if (causal) kend = min(kend, q0 + QT);
-  const int nkt = (kend + BK - 1) / BK;
+  const int nkt = (kend + BKT - 1) / BKT;
   // This workgroup's key tiles [t_lo, t_hi): all of them, or one of nsplit equal chunks (SPLIT:
   // unscaled float32 partial dQ rows go to part, [nsplit][BH*N][D], for bwd_sum_kernel).
   const int chunk = (nkt + nsp - 1) / nsp;
@@ -489,7 +536,7 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) dpart = frag_dot(frag_global<T>(rO, q, D, ks * M::KSTEP), of[ks], dpart);
     dq_ = dpart + swap_halves(dpart);
-    if (half == 0 && q < N && split == 0) Dv[(size_t)bh * N + q] = dq_;
+    if (half == 0 && q < N && split == 0 && grp == 0) Dv[(size_t)bh * N + q] = dq_;
   } else {
     dq_ = q < N ? Dv[(size_t)bh * N + q] : 0.f;
   }
@@ -506,8 +553,8 @@ __device__ __forceinline__ void dq_body(
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   if constexpr (DP > D) {
-    zero_pad_cols<T, BK, D, LD, DP, NT>(lds);
-    zero_pad_cols<T, BK, D, LD, DP, NT>(lds + 2 * TILE);
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds);
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 2 * TILE);
   }
   // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
   int cur = t_lo;
@@ -517,28 +564,29 @@ __device__ __forceinline__ void dq_body(
     cur = next_live_tile(map, t_lo, t_hi, SHIFT);
   }
   auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
-  TileCopy<T, BK, D, LD, NT> kc, vc;
+  TileCopy<T, BKT, D, LD, NT> kc, vc;
   if (cur < t_hi) {
-    kc.load(rk, cur * BK);
-    vc.load(rv, cur * BK);
+    kc.load(rk, cur * BKT);
+    vc.load(rv, cur * BKT);
     kc.store(lds);
     vc.store(lds + TILE);
   }
   __syncthreads();
   int nxt = cur < t_hi ? after(cur) : t_hi;
   if (nxt < t_hi) {
-    kc.load(rk, nxt * BK);
-    vc.load(rv, nxt * BK);
+    kc.load(rk, nxt * BKT);
+    vc.load(rv, nxt * BKT);
   }
   for (int it = 0; cur < t_hi; ++it) {
-    const lds_t* ktile = lds + (it & 1) * 2 * TILE;
+    // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
+    const lds_t* ktile = lds + (it & 1) * 2 * TILE + grp * BK * LD * (int)sizeof(T);
     const lds_t* vtile = ktile + TILE;
     bool run = wave_live;
     if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
     if (run) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int kb0 = cur * BK + nb * 32;
+        const int kb0 = cur * BKT + grp * BK + nb * 32;
         if (kb0 >= kend || (causal && kb0 > qw_last)) continue;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -572,11 +620,31 @@ __device__ __forceinline__ void dq_body(
     }
     __syncthreads();
     if (nxt2 < t_hi) {
-      kc.load(rk, nxt2 * BK);
-      vc.load(rv, nxt2 * BK);
+      kc.load(rk, nxt2 * BKT);
+      vc.load(rv, nxt2 * BKT);
     }
     cur = nxt;
     nxt = nxt2;
+  }
+
+  if constexpr (G == 2) {
+    // Group 1 hands its dQ sums to the wave of group 0 that owns the same queries (the tiles are
+    // no longer read: the loop ended on a barrier and staged nothing after it).
+    constexpr int F = NDB * 16;  // floats per lane
+    static_assert(NW * 64 * F * 4 <= 4 * TILE, "merge buffer fits in the tile stages");
+    float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mrg[(16 * i + e) * 64] = acc[i][e];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] += mrg[(16 * i + e) * 64];
   }
 
   if constexpr (SPLIT) {
@@ -622,15 +690,15 @@ __device__ __forceinline__ void dq_body(
   }
 }
 
-template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(
+template <typename T, int D, int NW, int BK, int OCC, bool BSP, bool SPLIT = false, int G = 1>
+__global__ __launch_bounds__(G * NW * 64, OCC) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ, int BH,
     int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
     const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, BK, BSP>()];
-  dq_body<T, D, NW, BK, BSP, SPLIT>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale,
-                                    scale_log2, kv_len, bmask, nsplit, part);
+  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, G * BK, BSP>()];
+  dq_body<T, D, NW, BK, BSP, SPLIT, G>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale,
+                                       scale_log2, kv_len, bmask, nsplit, part);
 }
 
 // out = scale * sum_s part[s] elementwise (fixed order, so the split backward stays deterministic),
@@ -686,8 +754,53 @@ __global__ __launch_bounds__(256, 2) void bwd_small_kernel(
                                                 causal, scale, scale_log2, kv_len, bmask);
 }
 
+// Dense masks: the same two kinds of work item on 8-wave workgroups whose two groups split each
+// item's chain (dq_body / dkdv_body with G = 2).  Such workgroups fit one per CU, fewer than the
+// items, so the items run longest first: `order` lists the item classes -- bit 7 set for dK/dV,
+// low bits the key tile (dK/dV) or the query tile counted from the end (dQ) -- by decreasing
+// expected time, and block b runs class b / BH for head b % BH.
+struct SmallOrder {
+  uint8_t cls[64];
+};
+
+// Block of a body's grid whose XCD-aware remap (xcd_logical_block) yields logical item L of n.
+__device__ __forceinline__ int block_of_logical(int L, int n) {
+  const int per = (n + 7) >> 3;
+  return (L % per) * 8 + L / per;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(512, 1) void bwd_small2_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ O, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ,
+    T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal, float scale, float scale_log2,
+    const int32_t* __restrict__ kv_len, SmallOrder order) {
+  __shared__ __attribute__((aligned(16))) char
+      smem[cmax(dq_lds_bytes<T, D, 64, false>(), dkdv_lds_bytes<T, D, 4, 64, true, false, 1, false, 2>())];
+  const int c = order.cls[blockIdx.x / BH], bh = blockIdx.x % BH;
+  const int T128 = (N + 127) / 128;  // query tiles of dQ items = key tiles of dK/dV items
+  if (c & 0x80)
+    dkdv_body<T, D, 4, 64, true, false, 1, false, false, 2>(
+        smem, block_of_logical(bh * T128 + (c & 0x7f), BH * T128), Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal,
+        scale, scale_log2, kv_len, nullptr);
+  else
+    dq_body<T, D, 4, 32, false, false, 2>(smem, block_of_logical(bh * T128 + c, BH * T128), Q, K, V, dO, O, Lse, Dv,
+                                          dQ, BH, H, N, causal, scale, scale_log2, kv_len, nullptr);
+}
+
 // ------------------------------------------------------------------------------------------
 // launchers
+
+// Two groups per workgroup in the backward kernels (G = 2 of dq_body and dkdv_body) where the
+// merged small-problem launch applies with a dense mask and chains are long enough to gain from
+// halving (N >= 512) -- also for the dQ and dK/dV kernels launched on their own, so that attn_bwd
+// and its sub-steps stay bitwise equal.  Measured on MI355X (backward launch, bf16): B=4 H=12
+// N=512 d=64 26.3 -> 22.7 us, B=2 H=16 N=1024 d=64 45.2 -> 39.2 us; at N=128 and 256 two groups
+// were slower (12.9 -> 17.9 us, 20.3 -> 22.1 us): their 8-wave workgroups fit one per CU, so the
+// items run in more than one round, which short chains do not pay back.
+static bool bwd_two_groups(int dtype, const Problem& p) {
+  return !p.bmask && p.N >= 512 && bwd_small_applies(dtype, p);
+}
 
 template <typename T, int D>
 static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* dO, float* Dv, hipStream_t s) {
@@ -724,6 +837,14 @@ static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, 
   }
   const int nlog = BH * TK;
   const int grid = (nlog + 7) / 8 * 8;
+  if constexpr (sizeof(T) == 2 && D <= 80 && NW == 4 && BQ == 64 && !VLDS && KB == 1) {
+    if (bwd_two_groups(kBF16, p)) {
+      hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, 1, VLDS, KB, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, s,
+                         (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, BH, p.H, p.N,
+                         p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr, 1, nullptr);
+      return hipGetLastError();
+    }
+  }
   if (p.bmask)
     hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, p.B * p.H, p.H, p.N, p.causal,
@@ -758,6 +879,14 @@ static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, co
   }
   const int nlog = BH * TQ;
   const int grid = (nlog + 7) / 8 * 8;
+  if constexpr (sizeof(T) == 2 && D <= 80 && NW == 4 && BK == 32) {
+    if (bwd_two_groups(kBF16, p)) {
+      hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, 1, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, s,
+                         (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, BH, p.H,
+                         p.N, p.causal, p.scale, p.scale * kLog2e, p.kv_len, nullptr, 1, nullptr);
+      return hipGetLastError();
+    }
+  }
   if (p.bmask)
     hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                        (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, p.B * p.H, p.H, p.N,
@@ -778,14 +907,46 @@ static hipError_t launch_bwd_small_t(const Problem& p, const void* Q, const void
   const int BH = p.B * p.H;
   const int nq = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
   const int nk = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
-  if (p.bmask)
-    hipLaunchKernelGGL((bwd_small_kernel<T, D, true>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
-                       (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
-                       p.scale, p.scale * kLog2e, p.kv_len, nq, p.bmask);
-  else
-    hipLaunchKernelGGL((bwd_small_kernel<T, D, false>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
-                       (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
-                       p.scale, p.scale * kLog2e, p.kv_len, nq, nullptr);
+  if (!bwd_two_groups(kBF16, p)) {
+    if (p.bmask)
+      hipLaunchKernelGGL((bwd_small_kernel<T, D, true>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
+                         (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N,
+                         p.causal, p.scale, p.scale * kLog2e, p.kv_len, nq, p.bmask);
+    else
+      hipLaunchKernelGGL((bwd_small_kernel<T, D, false>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,
+                         (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N,
+                         p.causal, p.scale, p.scale * kLog2e, p.kv_len, nq, nullptr);
+    return hipGetLastError();
+  }
+  // Item classes, longest expected time first.  Per-item times measured on MI355X (two groups,
+  // d = 64): dK/dV about 5 us + 2.7 us per 128-query stage, dQ about 5.2 us + 0.8 us per
+  // 64-key tile.  Ties keep dK/dV before dQ and lower tiles first.
+  const int T128 = (p.N + 127) / 128;
+  if (2 * T128 > 64) return hipErrorInvalidValue;
+  struct Cls { float cost; int key; uint8_t code; } cls[64];
+  int nc = 0;
+  for (int kt = 0; kt < T128; ++kt) {
+    const int stages = p.causal ? T128 - kt : T128;
+    cls[nc] = {5.0f + 2.7f * stages, nc, (uint8_t)(0x80 | kt)};
+    ++nc;
+  }
+  for (int r = 0; r < T128; ++r) {  // r-th query tile from the end
+    const int qt = T128 - 1 - r;
+    const int keys = p.causal ? (p.N < 128 * (qt + 1) ? p.N : 128 * (qt + 1)) : p.N;
+    cls[nc] = {5.2f + 0.8f * ((keys + 63) / 64), nc, (uint8_t)r};
+    ++nc;
+  }
+  for (int i = 1; i < nc; ++i)  // insertion sort by decreasing cost, stable
+    for (int j = i; j > 0 && cls[j].cost > cls[j - 1].cost; --j) {
+      const Cls t = cls[j];
+      cls[j] = cls[j - 1];
+      cls[j - 1] = t;
+    }
+  SmallOrder order{};
+  for (int i = 0; i < nc; ++i) order.cls[i] = cls[i].code;
+  hipLaunchKernelGGL((bwd_small2_kernel<T, D>), dim3(nc * BH), dim3(512), 0, s, (const T*)Q, (const T*)K,
+                     (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, (T*)dK, (T*)dV, BH, p.H, p.N, p.causal,
+                     p.scale, p.scale * kLog2e, p.kv_len, order);
   return hipGetLastError();
 }
 

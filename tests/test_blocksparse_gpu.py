@@ -82,10 +82,10 @@ def test_blocksparse_matches_oracle(B, H, N, d, dtype, causal, kv, density, head
         assert torch.all(torch.isneginf(L[:, :, 64:128]))
 
 
-# Shapes whose dense forward runs the same tiling as the block-sparse one: one key group per
-# workgroup (bf16 grids of at most 256 query tiles with N >= 256 use two, which add the two halves
-# of every row in another order).
-@pytest.mark.parametrize("N,d,dtype,causal,BH", [(200, 64, "bf16", True, 2), (257, 128, "f32", False, 2),
+# Shapes whose dense kernels run the same tiling as the block-sparse ones: one key or query group
+# per workgroup (small bf16 grids use two for dense masks, which add the two halves of every sum in
+# another order).
+@pytest.mark.parametrize("N,d,dtype,causal,BH", [(300, 64, "bf16", True, 100), (257, 128, "f32", False, 2),
                                                   (1024, 64, "bf16", True, 40), (1024, 128, "bf16", True, 128)])
 def test_all_ones_mask_equals_dense_bitwise(N, d, dtype, causal, BH):
     inp = make_inputs(1, BH, N, d, dtype, seed=3)
