@@ -34,13 +34,18 @@ SMALL += [
     ("bf16", 1, 2, 130, 128, False, None),
     ("f32", 1, 2, 96, 64, False, [50]),
     # forward with two key groups per workgroup (grids of at most 256 query tiles, N >= 256) and
-    # either side of that threshold
+    # either side of that threshold; the first 64-head case also runs the two-group backward, the
+    # 65-head one the plain two-kernel backward
     ("bf16", 2, 3, 700, 128, True, [650, 700]),
     ("bf16", 1, 2, 520, 80, True, [400]),
     ("bf16", 1, 2, 333, 32, True, None),
     ("bf16", 1, 2, 300, 16, False, [70]),
     ("bf16", 1, 64, 512, 64, True, None),
     ("bf16", 1, 65, 512, 64, True, None),
+    # backward with two groups per workgroup (small bf16 grids, d <= 80, N >= 512, dense mask)
+    ("bf16", 1, 2, 600, 32, True, [550]),
+    ("bf16", 2, 1, 513, 16, False, None),
+    ("bf16", 1, 3, 1100, 64, False, [1000]),
 ]
 
 
