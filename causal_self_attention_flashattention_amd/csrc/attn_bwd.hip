@@ -109,7 +109,7 @@ __device__ __forceinline__ void dkdv_body(
 
   const int TK = (N + KT - 1) / KT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = xcd_logical_block(BH * TK * nsp, block);
+  const int logical = rank_major_block(BH, TK * nsp, block);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TK;
@@ -485,7 +485,7 @@ __device__ __forceinline__ void dq_body(
 
   const int TQ = (N + QT - 1) / QT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = xcd_logical_block(BH * TQ * nsp, block);
+  const int logical = rank_major_block(BH, TQ * nsp, block);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TQ;
@@ -763,11 +763,6 @@ struct SmallOrder {
   uint8_t cls[64];
 };
 
-// Block of a body's grid whose XCD-aware remap (xcd_logical_block) yields logical item L of n.
-__device__ __forceinline__ int block_of_logical(int L, int n) {
-  const int per = (n + 7) >> 3;
-  return (L % per) * 8 + L / per;
-}
 
 template <typename T, int D>
 __global__ __launch_bounds__(512, 1) void bwd_small2_kernel(
@@ -777,14 +772,15 @@ __global__ __launch_bounds__(512, 1) void bwd_small2_kernel(
     const int32_t* __restrict__ kv_len, SmallOrder order) {
   __shared__ __attribute__((aligned(16))) char
       smem[cmax(dq_lds_bytes<T, D, 64, false>(), dkdv_lds_bytes<T, D, 4, 64, true, false, 1, false, 2>())];
-  const int c = order.cls[blockIdx.x / BH], bh = blockIdx.x % BH;
-  const int T128 = (N + 127) / 128;  // query tiles of dQ items = key tiles of dK/dV items
+  const int c = order.cls[blockIdx.x / BH];
+  // Block of the bodies' rank-major grids: rank (c & 0x7f) of head blockIdx.x % BH.
+  const int b = (c & 0x7f) * BH + (int)blockIdx.x % BH;
   if (c & 0x80)
     dkdv_body<T, D, 4, 64, true, false, 1, false, false, 2>(
-        smem, block_of_logical(bh * T128 + (c & 0x7f), BH * T128), Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal,
+        smem, b, Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal,
         scale, scale_log2, kv_len, nullptr);
   else
-    dq_body<T, D, 4, 32, false, false, 2>(smem, block_of_logical(bh * T128 + c, BH * T128), Q, K, V, dO, O, Lse, Dv,
+    dq_body<T, D, 4, 32, false, false, 2>(smem, b, Q, K, V, dO, O, Lse, Dv,
                                           dQ, BH, H, N, causal, scale, scale_log2, kv_len, nullptr);
 }
 
@@ -819,7 +815,7 @@ static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, 
   const int TK = (p.N + KT - 1) / KT;
   const int BH = p.B * p.H;
   if (nsplit > 1) {
-    const int grid = (BH * TK * nsplit + 7) / 8 * 8;
+    const int grid = BH * TK * nsplit;
     if (p.bmask)
       hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, OCC, VLDS, KB, true, true>), dim3(grid), dim3(NW * 64), 0, s,
                          (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, (T*)dK, (T*)dV, BH, p.H, p.N,
@@ -835,8 +831,7 @@ static hipError_t launch_dkdv_t(const Problem& p, const void* Q, const void* K, 
     if (e != hipSuccess) return e;
     return launch_sum<T>(part + (size_t)nsplit * count, nsplit, count, 1.0f, dV, s);
   }
-  const int nlog = BH * TK;
-  const int grid = (nlog + 7) / 8 * 8;
+  const int grid = BH * TK;
   if constexpr (sizeof(T) == 2 && D <= 80 && NW == 4 && BQ == 64 && !VLDS && KB == 1) {
     if (bwd_two_groups(kBF16, p)) {
       hipLaunchKernelGGL((dkdv_kernel<T, D, NW, BQ, 1, VLDS, KB, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, s,
@@ -864,7 +859,7 @@ static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, co
   const int TQ = (p.N + QT - 1) / QT;
   const int BH = p.B * p.H;
   if (nsplit > 1) {
-    const int grid = (BH * TQ * nsplit + 7) / 8 * 8;
+    const int grid = BH * TQ * nsplit;
     if (p.bmask)
       hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, OCC, true, true>), dim3(grid), dim3(NW * 64), 0, s, (const T*)Q,
                          (const T*)K, (const T*)V, (const T*)dO, (const T*)O, L, Dv, (T*)dQ, BH, p.H, p.N, p.causal,
@@ -877,8 +872,7 @@ static hipError_t launch_dq_t(const Problem& p, const void* Q, const void* K, co
     if (e != hipSuccess) return e;
     return launch_sum<T>(part, nsplit, (size_t)BH * p.N * D, p.scale, dQ, s);
   }
-  const int nlog = BH * TQ;
-  const int grid = (nlog + 7) / 8 * 8;
+  const int grid = BH * TQ;
   if constexpr (sizeof(T) == 2 && D <= 80 && NW == 4 && BK == 32) {
     if (bwd_two_groups(kBF16, p)) {
       hipLaunchKernelGGL((dq_kernel<T, D, NW, BK, 1, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, s,
@@ -905,8 +899,8 @@ static hipError_t launch_bwd_small_t(const Problem& p, const void* Q, const void
                                      const void* O, const float* L, float* Dv, void* dQ, void* dK, void* dV,
                                      hipStream_t s) {
   const int BH = p.B * p.H;
-  const int nq = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
-  const int nk = (BH * ((p.N + 127) / 128) + 7) / 8 * 8;
+  const int nq = BH * ((p.N + 127) / 128);
+  const int nk = nq;
   if (!bwd_two_groups(kBF16, p)) {
     if (p.bmask)
       hipLaunchKernelGGL((bwd_small_kernel<T, D, true>), dim3(nq + nk), dim3(256), 0, s, (const T*)Q, (const T*)K,

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 
   const int TQ = (N + QT - 1) / QT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = xcd_logical_block(BH * TQ * nsp);
+  const int logical = rank_major_block(BH, TQ * nsp, blockIdx.x);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TQ;
@@ -357,7 +357,7 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   const float sl2 = p.scale * kLog2e;
   const int BH = p.B * p.H;
   if (nsplit > 1) {
-    const int grid = (BH * TQ * nsplit + 7) / 8 * 8;
+    const int grid = BH * TQ * nsplit;
     if (p.bmask)
       hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true, true>), dim3(grid), dim3(NW * 64), 0, stream,
                          (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
@@ -374,7 +374,7 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
                        (const float*)part, nsplit, rows, (T*)O, L);
     return hipGetLastError();
   }
-  const int grid = (BH * TQ + 7) / 8 * 8;
+  const int grid = BH * TQ;
   if constexpr (sizeof(T) == 2 && BK == 64) {
     if (!p.bmask && fwd_two_groups(p, BH * TQ)) {
       hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, 1, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, stream,
