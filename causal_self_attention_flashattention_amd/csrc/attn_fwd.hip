@@ -342,9 +342,9 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
 
 // Two key groups per workgroup (fwd_kernel's G = 2) when the grid of 128-query workgroups is at
 // most one per CU and the longest key chain has at least four 64-key tiles: each CU then runs
-// one workgroup, whose chain the second group halves.  Measured on MI355X: B=4 H=12 N=512 d=64
-// 11.1 -> 10.5 us, B=2 H=16 N=1024 d=64 18.1 -> 16.1 us (64-query workgroups with two groups,
-// two per CU, were slower than these).
+// one workgroup, whose chain the second group halves.  Measured on MI355X with the heaviest-first
+// work order: B=4 H=12 N=512 d=64 11.1 -> 9.4 us, B=2 H=16 N=1024 d=64 18.1 -> 14.2 us (with
+// 64-query workgroups, two per CU, at d <= 64; 128-query ones gave 10.5 and 16.2 us).
 static bool fwd_two_groups(const Problem& p, long items) {
   return items <= 256 && p.N >= 256;
 }
@@ -377,9 +377,13 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   const int grid = BH * TQ;
   if constexpr (sizeof(T) == 2 && BK == 64) {
     if (!p.bmask && fwd_two_groups(p, BH * TQ)) {
-      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, 1, false, false, 2>), dim3(grid), dim3(2 * NW * 64), 0, stream,
-                         (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
-                         nullptr, 1, nullptr);
+      // Up to d = 64 two such workgroups fit a CU: 64-query workgroups then spread the heaviest
+      // query tiles over twice as many CUs.
+      constexpr int NW2 = D <= 64 ? 2 : NW;
+      const int grid2 = BH * ((p.N + 32 * NW2 - 1) / (32 * NW2));
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW2, BK, D <= 64 ? 2 : 1, false, false, 2>), dim3(grid2),
+                         dim3(2 * NW2 * 64), 0, stream, (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H,
+                         p.N, p.causal, sl2, p.kv_len, nullptr, 1, nullptr);
       return hipGetLastError();
     }
   }
