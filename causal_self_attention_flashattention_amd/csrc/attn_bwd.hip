@@ -121,8 +121,8 @@ __device__ __forceinline__ void dkdv_body(
   const size_t base = (size_t)bh * N * D;
   dK += base; dV += base;
 
-  const int grp = (int)(threadIdx.x >> 6) / NW;  // query group (G = 2) or 0
-  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = G == 1 ? 0 : (int)(threadIdx.x >> 6) / NW;  // query group (G = 2) or 0
+  const int w = G == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int k0 = kt * KT;
   const int kw = k0 + KW * w;  // first key of this wave
   const bool wave_live = kw < kv;
@@ -156,13 +156,18 @@ __device__ __forceinline__ void dkdv_body(
         kf[kb][ks] = frag_global<T>(rk, kw + 32 * kb + col, D, ks * M::KSTEP);
         if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
       }
+    auto settle_kv = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        settle(kf[kb][ks]);
-        if constexpr (!VLDS) settle(vf[kb][ks]);
-      }
+        for (int ks = 0; ks < KS; ++ks) {
+          settle(kf[kb][ks]);
+          if constexpr (!VLDS) settle(vf[kb][ks]);
+        }
+    };
+    // Without DSELF the fragments are waited for here (keeping them out of the first stage's
+    // register peak); with DSELF only after the D rows, whose loads then overlap theirs.
+    if constexpr (!DSELF) settle_kv();
     const int TQ = (N + BQS - 1) / BQS;
     const int qt0 = causal ? k0 / BQS : 0;
     // This workgroup's query tiles [qt_lo, qt_hi): all from qt0, or one of nsplit equal chunks.
@@ -172,26 +177,6 @@ __device__ __forceinline__ void dkdv_body(
 
     // DSELF: D for rows [qt0*BQS, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
-    if constexpr (DSELF) {
-      for (int r = qt0 * BQS + threadIdx.x; r < N; r += NT) {
-        const T* orow = Oin + base + (size_t)r * D;
-        const T* grow = dO + base + (size_t)r * D;
-        float part[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          part[h] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            typename M::frag a, g;
-            __builtin_memcpy(&a, orow + ks * M::KSTEP + M::KPL * h, sizeof(a));
-            __builtin_memcpy(&g, grow + ks * M::KSTEP + M::KPL * h, sizeof(g));
-            part[h] = frag_dot(a, g, part[h]);
-          }
-        }
-        dself[r - qt0 * BQS] = -(part[0] + part[1]);
-      }
-    }
-
     if constexpr (DP > D) {
       zero_pad_cols<T, BQS, D, LD, DP, NT>(lds);
       zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + TILE);
@@ -227,7 +212,30 @@ __device__ __forceinline__ void dkdv_body(
       cur = next_live_tile(map, qt_lo, qt_hi, SHIFT);
     }
     auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, qt_hi, SHIFT) : t + 1; };
-    if (cur < qt_hi) {
+    if constexpr (DSELF) {
+      // The first stage's loads, the D row loads and the K/V fragments are all in flight before
+      // the first wait, so this prologue costs one memory latency rather than three.
+      if (cur < qt_hi) load_stage(cur);
+      for (int r = qt0 * BQS + threadIdx.x; r < N; r += NT) {
+        const T* orow = Oin + base + (size_t)r * D;
+        const T* grow = dO + base + (size_t)r * D;
+        float part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          part[h] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            typename M::frag a, g;
+            __builtin_memcpy(&a, orow + ks * M::KSTEP + M::KPL * h, sizeof(a));
+            __builtin_memcpy(&g, grow + ks * M::KSTEP + M::KPL * h, sizeof(g));
+            part[h] = frag_dot(a, g, part[h]);
+          }
+        }
+        dself[r - qt0 * BQS] = -(part[0] + part[1]);
+      }
+      settle_kv();
+      if (cur < qt_hi) store_stage(lds);
+    } else if (cur < qt_hi) {
       load_stage(cur);
       store_stage(lds);
     }
@@ -497,8 +505,8 @@ __device__ __forceinline__ void dq_body(
   const size_t base = (size_t)bh * N * D;
   dQ += base;
 
-  const int grp = (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
-  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = G == 1 ? 0 : (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
+  const int w = G == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int q0 = qt * QT;
   const int qw = q0 + 32 * w;
   const int q = qw + col;
@@ -529,6 +537,30 @@ __device__ __forceinline__ void dq_body(
     of[ks] = frag_global<T>(ro, q, D, ks * M::KSTEP);
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : 0.f;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+
+  if constexpr (DP > D) {
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds);
+    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 2 * TILE);
+  }
+  // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
+  int cur = t_lo;
+  if constexpr (BSP) {
+    build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
+    __syncthreads();
+    cur = next_live_tile(map, t_lo, t_hi, SHIFT);
+  }
+  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
+  // The first K/V tile's loads are issued before D waits on its O fragments, so the prologue
+  // costs one memory latency rather than two.
+  TileCopy<T, BKT, D, LD, NT> kc, vc;
+  if (cur < t_hi) {
+    kc.load(rk, cur * BKT);
+    vc.load(rv, cur * BKT);
+  }
   float dq_;
   if (Oin) {
     const auto rO = make_rsrc(Oin + base, tbytes);
@@ -547,27 +579,7 @@ __device__ __forceinline__ void dq_body(
   }
   settle(lq);
   settle(dq_);
-
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-
-  if constexpr (DP > D) {
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds);
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 2 * TILE);
-  }
-  // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
-  int cur = t_lo;
-  if constexpr (BSP) {
-    build_tile_map(map, bmask, (N + kMaskBlock - 1) / kMaskBlock, q0 / kMaskBlock, QT / kMaskBlock, false, NT);
-    __syncthreads();
-    cur = next_live_tile(map, t_lo, t_hi, SHIFT);
-  }
-  auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
-  TileCopy<T, BKT, D, LD, NT> kc, vc;
   if (cur < t_hi) {
-    kc.load(rk, cur * BKT);
-    vc.load(rv, cur * BKT);
     kc.store(lds);
     vc.store(lds + TILE);
   }

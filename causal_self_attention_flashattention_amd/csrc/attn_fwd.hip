@@ -79,8 +79,8 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   O += base;
   Lse += (size_t)bh * N;
 
-  const int grp = (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
-  const int w = (threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
+  const int grp = G == 1 ? 0 : (int)(threadIdx.x >> 6) / NW;  // key group (G = 2) or 0
+  const int w = G == 1 ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 6) % NW, l = lane_id(), half = l >> 5, col = l & 31;
   const int q0 = qt * QT;
   const int qw = q0 + 32 * w;  // first query of this wave
   const int q = qw + col;      // this lane's query
