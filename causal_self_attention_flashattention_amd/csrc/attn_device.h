@@ -80,6 +80,17 @@ template <> struct Mfma<__bf16> {
     for (int s = 0; s < 8; ++s) f[s] = (__bf16)a[8 * c + s];
     return f;
   }
+  // acc + the sum of the 8 elements, two per v_dot2 against (1, 1) with fp32 accumulation.
+  __device__ __forceinline__ static float frag_sum(const frag& f, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x2 pr = {f[2 * t], f[2 * t + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
+  }
   // Operand straight from global memory (row r of a row-major matrix, columns col0..col0+7).
   __device__ __forceinline__ static frag load_global(const __bf16* rowp, int col0, bool valid) {
     frag f = {};
@@ -108,6 +119,7 @@ template <> struct Mfma<float> {
     return *reinterpret_cast<const __attribute__((address_space(3))) float*>(tile + 4 * (off + row * ld + (l & 31)));
   }
   __device__ __forceinline__ static frag acc_frag(const f32x16& a, int c) { return a[c]; }
+  __device__ __forceinline__ static float frag_sum(frag f, float acc) { return acc + f; }
   __device__ __forceinline__ static frag load_global(const float* rowp, int col0, bool valid) {
     return valid ? rowp[col0 + (lane_id() >> 5)] : 0.0f;
   }

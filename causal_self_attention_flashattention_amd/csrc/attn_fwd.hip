@@ -23,6 +23,10 @@
 namespace attn {
 
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kSumBound = 256.0f;  // 2^kRescaleSlack
+// Head dims up to 64, where the softmax's vector work per key outweighs the matrix products, form
+// the weights before taking the row max (see the tile loop); larger ones take the max first.
+constexpr int kSumCheckMaxD = 64;
 
 // With SPLIT the key range of every query tile is cut into `nsplit` chunks, one workgroup each;
 // a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
@@ -105,13 +109,12 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   typename M::frag qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_part = 0.f;
+  bool first = true;  // no tile run yet: the running max starts from the first tile's max
 
   if constexpr (DP > D) {
     zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + TILE);
@@ -130,6 +133,12 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   if (cur < t_hi) {
     kc.load(rk, cur * BKT);
     vc.load(rv, cur * BKT);
+  }
+  // The Q fragments were requested first: waiting for them here leaves the first K/V tile's loads
+  // in flight, so the two memory latencies overlap.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+  if (cur < t_hi) {
     kc.store(lds);
     vc.store(lds + TILE);
   }
@@ -149,55 +158,99 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     bool run = wave_live && k0 < kend && !(causal && k0 > qw_last);
     if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
     if (run) {
+      // Scores of this wave's keys of the tile (raw, unscaled); masked ones replaced (only on
+      // tiles that cross the diagonal or the key end).
       f32x16 s[NB];
+      auto scores = [&](const lds_t* kt) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        s[nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) {
+          s[nb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[nb] = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
-      }
-      // Raw scores; masked ones replaced (only on tiles that cross the diagonal or the key end).
-      if ((causal && k0 + BK - 1 > qw) || k0 + BK > kv) {
+          for (int ks = 0; ks < KS; ++ks)
+            s[nb] = M::mma(M::frag_direct(kt, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+        }
+        if ((causal && k0 + BK - 1 > qw) || k0 + BK > kv) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              s[nb][e] = (k0 + nb * 32 + acc_row(e, half) > lim) ? kMaskedScore : s[nb][e];
+        }
+      };
+      // Row max of key blocks [nb0, nb1); the running max moves (and O, l are rescaled) when it
+      // exceeds the running max by more than the slack.
+      auto move_max = [&](int nb0, int nb1) {
+        float mx = s[nb0][0];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
+          if (nb >= nb0 && nb < nb1)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            s[nb][e] = (k0 + nb * 32 + acc_row(e, half) > lim) ? kMaskedScore : s[nb][e];
-      }
-      float mx = s[0][0];
+            for (int e = (nb == nb0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
+        mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+        if (mx > m_run + kRescaleSlack) {
+          const float alpha = fast_exp2(m_run - mx);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+          for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int e = (nb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
-      mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
-      if (mx > m_run + kRescaleSlack) {
-        const float alpha = fast_exp2(m_run - mx);
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-        l_part *= alpha;
-        m_run = mx;
-      }
-      const float neg_m = -m_run;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, neg_m));
-          s[nb][e] = p;
-          l_part += p;
+            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+          l_part *= alpha;
+          m_run = mx;
         }
+      };
+      // Unnormalised weights 2^(s scale_log2 - m_run) of key block nb as MFMA operands, and this
+      // lane's part of their row sum (bf16: the sum of the rounded weights the product uses, two
+      // per dot2).
+      typename M::frag pf[M::CALLS32];
+      float lsum;
+      auto weights = [&](int nb) {
+        const float neg_m = -m_run;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int e = 0; e < 16; ++e) s[nb][e] = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, neg_m));
+        lsum = 0.f;
 #pragma unroll
         for (int c = 0; c < M::CALLS32; ++c) {
-          const typename M::frag pf = M::acc_frag(s[nb], c);
+          pf[c] = M::acc_frag(s[nb], c);
+          lsum = M::frag_sum(pf[c], lsum);
+        }
+      };
+      scores(ktile);
+      // Head dims above kSumCheckMaxD, and a wave's first tile, take the tile's row max first.
+      // Otherwise each key block's weights are formed with the running max as it stands: a lane whose weights sum to
+      // at most 2^kRescaleSlack has every weight within that bound, which is all the running max
+      // must guarantee, so the block's max is only taken (and the max moved) when some lane
+      // exceeds it or overflowed -- the scores of that block are then recomputed.
+      const bool check = !first && D <= kSumCheckMaxD;
+      if (first || D > kSumCheckMaxD) {
+        move_max(0, NB);
+        first = false;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        weights(nb);
+        if (check && __ballot(!(lsum <= kSumBound)) != 0) {
+          // Re-read the K fragments rather than keep the first reads live through the fast path.
+          int fresh = 0;
+          asm volatile("" : "+v"(fresh));
+          const lds_t* kt = ktile + fresh;
+          s[nb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            s[nb] = M::mma(M::frag_direct(kt, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+          if ((causal && k0 + BK - 1 > qw) || k0 + BK > kv) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              s[nb][e] = (k0 + nb * 32 + acc_row(e, half) > lim) ? kMaskedScore : s[nb][e];
+          }
+          move_max(nb, nb + 1);
+          weights(nb);
+        }
+        l_part += lsum;
+#pragma unroll
+        for (int c = 0; c < M::CALLS32; ++c)
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf, o[db]);
-        }
+            o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf[c], o[db]);
+      }
     }
     const int nxt2 = nxt < t_hi ? after(nxt) : t_hi;
     if (nxt < t_hi) {
@@ -432,9 +485,9 @@ hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K,
   float* part = (float*)workspace;
   if (dtype == kBF16) {
     switch (p.d) {
-      case 16: return launch_fwd_t<__bf16, 16, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
-      case 32: return launch_fwd_t<__bf16, 32, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
-      case 64: return launch_fwd_t<__bf16, 64, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      case 16: return launch_fwd_t<__bf16, 16, 4, 64, 4>(p, Q, K, V, O, L, s, ns, part);
+      case 32: return launch_fwd_t<__bf16, 32, 4, 64, 4>(p, Q, K, V, O, L, s, ns, part);
+      case 64: return launch_fwd_t<__bf16, 64, 4, 64, 4>(p, Q, K, V, O, L, s, ns, part);
       case 80: return launch_fwd_t<__bf16, 80, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
       case 128: return launch_fwd_t<__bf16, 128, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
     }
