@@ -16,7 +16,7 @@ import torch
 
 from causal_self_attention_flashattention_amd.inputs import WORKLOADS, make_inputs, make_workload_inputs
 
-from attn_testutil import announce, compare_all, oracle_ref, require_gpu, run_gpu, to_dev
+from attn_testutil import announce, check_close, compare_all, heads_to_numpy, oracle_ref, require_gpu, run_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,80 @@ def test_workload_matches_oracle(name):
     ref = oracle_ref(inp, w.causal, w.scale, heads)
     rep = compare_all(res, ref, w.dtype, heads)
     announce(f"workload {name} max abs / rel errors: " + ", ".join(f"{k}={v[0]:.3g}/{v[1]:.3g}" for k, v in rep.items()))
+
+
+# Scores that climb along the key index (a ramp) or jump at scattered keys (spikes), so the
+# forward's running row max has to move on many 32-key blocks: this exercises the rescaling of
+# the output accumulator and row sum, and (head dims up to 64) the path that recomputes a key
+# block's scores when its weights, formed with the stale max, sum past the bound.  Every query
+# gets 4 added to each feature and every key c_j (all features), which lifts score (i, j) by about
+# 4 d c_j: c_j rises by `lift` log2 units of the scaled score per key (ramp), or jumps by 12 units
+# at one key in ten (spikes).  Spreading the pattern over all features keeps every key feature
+# small; a pattern carried by one feature alone makes that feature large, and dQ's products with
+# bf16-rounded dS then lose more than the tolerance to cancellation (sum_j dS_ij = 0).
+RISING = [
+    ("bf16", 1, 2, 300, 64, True, None),
+    ("bf16", 1, 2, 300, 128, True, [280]),
+    ("bf16", 1, 2, 300, 80, False, None),
+    ("f32", 1, 2, 200, 64, False, [150]),
+    ("f32", 1, 1, 160, 128, True, None),
+    ("bf16", 1, 2, 520, 64, True, None),
+    ("bf16", 2, 3, 700, 128, True, None),
+    ("bf16", 1, 1, 2048, 64, True, None),
+]
+
+
+@pytest.mark.parametrize("pattern", ["ramp", "spikes"])
+@pytest.mark.parametrize("dtype,B,H,N,d,causal,kv", RISING, ids=lambda x: str(x))
+def test_rising_scores_move_the_running_max(pattern, dtype, B, H, N, d, causal, kv):
+    require_gpu()
+    seed = 3000 + N + d
+    announce(f"rising-{pattern} dtype={dtype} B={B} H={H} N={N} d={d} causal={causal} kv={kv} seed={seed}")
+    inp = make_inputs(B, H, N, d, dtype, seed, kv_len=kv)
+    scale = 1.0 / math.sqrt(d)
+    a = 4.0
+    unit = 1.0 / (scale * math.log2(math.e) * a * d)  # key lift per log2 unit of scaled score
+    if pattern == "ramp":
+        lift = 0.35 if N <= 1024 else 0.06
+        c = lift * unit * torch.arange(N, dtype=torch.float32)
+    else:
+        g = torch.Generator("cpu").manual_seed(seed)
+        c = (torch.rand(N, generator=g) < 0.1).float() * (12.0 * unit)
+    q = inp["q"].float() + a
+    k = inp["k"].float() + c[:, None]
+    inp["q"], inp["k"] = q.to(inp["v"].dtype), k.to(inp["v"].dtype)
+    res = run_gpu(to_dev(inp), causal, scale)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_ref(inp, causal, scale, heads)
+    # O, L and D to the usual bounds.  The gradients also carry, to first order, errors that these
+    # peaked weights make larger than the plain bound allows: P and dS enter the products rounded
+    # to bf16 (2^-9 relative each), P is recomputed from L, whose row sum adds up the rounded
+    # weights (up to 2^-9 relative in P), and D is formed from the stored, rounded O (|dD_i| <=
+    # D_slack_i).  With eps = 2^-8 that gives |dV_j - ref| <= eps sum_i P_ij |dO_i| and, through
+    # |d dS_ij| <= eps P_ij |dP_ij - D_i| + P_ij dD_i, the dQ and dK terms below -- a bound a
+    # wrong term or index would exceed by far.  float32 runs keep the plain bound.
+    for key in ("O", "L", "D"):
+        check_close(key, heads_to_numpy(res[key], heads), ref[key], dtype,
+                    ref["D_slack"] if key == "D" else 0.0)
+    qn, kn = inp["q"].double().numpy(), inp["k"].double().numpy()
+    vn, don = inp["v"].double().numpy(), inp["do"].double().numpy()
+    sl = {key: np.zeros(qn.shape) for key in ("dQ", "dK", "dV")}
+    kvl = None if kv is None else list(kv)
+    if dtype == "bf16":
+        eps = 2.0 ** -8
+        for b, h in heads:
+            S = scale * qn[b, h] @ kn[b, h].T
+            i, j = np.indices(S.shape)
+            valid = np.ones(S.shape, dtype=bool)
+            if causal:
+                valid &= j <= i
+            if kvl is not None:
+                valid &= j < kvl[b]
+            P = np.where(valid, np.exp(np.where(valid, S, 0.0) - ref["L"][b, h][:, None]), 0.0)
+            dP = don[b, h] @ vn[b, h].T
+            dds = eps * P * np.abs(dP - ref["D"][b, h][:, None]) + P * ref["D_slack"][b, h][:, None]
+            sl["dV"][b, h] = eps * (P.T @ np.abs(don[b, h]))
+            sl["dQ"][b, h] = scale * (dds @ np.abs(kn[b, h]))
+            sl["dK"][b, h] = scale * (dds.T @ np.abs(qn[b, h]))
+    for key in ("dQ", "dK", "dV"):
+        check_close(key, heads_to_numpy(res[key], heads), ref[key], dtype, sl[key])
