@@ -133,6 +133,37 @@ def copy_probe(nbytes: int, reps: int) -> None:
                       "GB/s (read+write)": 2 * nbytes / dt / 1e9}), flush=True)
 
 
+def rowdot_bench(args, w, lib, P_, B, H, N, d, dt, stream, step_binding):
+    """Time attn_bwd_rowdot alone: it reads O and dO once and writes D (HBM-bound, no reuse)."""
+    import torch
+
+    step_binding()  # O (and L) from the forward, as the pass sees them in the backward
+    for _ in range(args.warmup):
+        lib.attn_bwd_rowdot(P_["o"], P_["do"], P_["D"], B, H, N, d, dt, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    st = 0
+    for _ in range(args.steps):
+        st |= lib.attn_bwd_rowdot(P_["o"], P_["do"], P_["D"], B, H, N, d, dt, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    if st != 0:
+        raise RuntimeError(f"attn_bwd_rowdot failed with status {st}")
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = 2 * B * H * N * d * es + 4 * B * H * N
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "D = rowsum(O o dO) pass, HBM GB/s", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "us_per_launch": us, "higher_is_better": True,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "bytes_per_launch": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "rowdot"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +175,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the per-kernel HIP events on every n-th timed step (1 = every step)")
+    ap.add_argument("--rowdot", action="store_true",
+                    help="instead of the attention step, time the stand-alone D = rowsum(O o dO) pass "
+                         "(attn_bwd_rowdot) on the workload's O and dO and report HBM GB/s")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the attention step, time a plain device-to-device copy of this many bytes "
                          "(the reference kernel that HBM byte counters are scaled against)")
@@ -193,6 +227,10 @@ def main():
     def step_binding():
         attn.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_len=kvd, out=o, lse=L)
         attn.bwd(q, k, v, o, do, L, causal=w.causal, scale=w.scale, kv_len=kvd, outs=(dq, dk, dv, D))
+
+    if args.rowdot:
+        rowdot_bench(args, w, lib, P_, B, H, N, d, dt, stream, step_binding)
+        return
 
     fused = attn.bwd_launches(B, H, N, d, q.dtype) == 1
     KERNELS = KERNELS_FUSED if fused else KERNELS_SPLIT

@@ -24,28 +24,50 @@ namespace attn {
 // ------------------------------------------------------------------------------------------
 // D = rowsum(O o dO)
 
+// Rows of O and dO staged per workgroup: read with contiguous 16-byte loads (consecutive lanes,
+// consecutive chunks of a row), so every HBM line is fetched once, then reduced from LDS.
+constexpr int kRowdotRows = 128;
+
+template <typename T, int D>
+constexpr int rowdot_pitch() { return D + 16 / (int)sizeof(T); }  // one 16-byte chunk of padding per row
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                      float* __restrict__ Dv, int rows) {
-  // Thread pair (2i, 2i+1) owns row i; thread `half` of the pair reduces the columns an MFMA operand
-  // fragment of that half holds (fragments ks = 0.. in order), then the two halves are added.
+  // Thread pair (2i, 2i+1) owns row i of the workgroup's block; thread `half` of the pair reduces
+  // the columns an MFMA operand fragment of that half holds (fragments ks = 0.. in order), then the
+  // two halves are added -- the order the dQ kernel uses for the same rows, so D agrees bitwise.
   using M = Mfma<T>;
   constexpr int KS = D / M::KSTEP;
-  const int half = threadIdx.x & 1;
-  for (int row = (blockIdx.x * 256 + threadIdx.x) >> 1; row < rows; row += gridDim.x * 128) {
-    const T* orow = O + (size_t)row * D + M::KPL * half;
-    const T* grow = dO + (size_t)row * D + M::KPL * half;
-    float part = 0.f;
+  constexpr int R = kRowdotRows;
+  constexpr int LDP = rowdot_pitch<T, D>();
+  constexpr int TILE = R * LDP * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
+  lds_t* lds = (lds_t*)smem;
+  const int r0 = blockIdx.x * R;
+  const int nr = min(R, rows - r0);
+  const uint32_t bytes = (uint32_t)(nr * D * (int)sizeof(T));  // rows past the end read as zero
+  const auto ro = make_rsrc(O + (size_t)r0 * D, bytes);
+  const auto rg = make_rsrc(dO + (size_t)r0 * D, bytes);
+  TileCopy<T, R, D, LDP, 256> oc, gc;
+  oc.load(ro, 0);
+  gc.load(rg, 0);
+  oc.store(lds);
+  gc.store(lds + TILE);
+  __syncthreads();
+  const int half = threadIdx.x & 1, row = threadIdx.x >> 1;
+  typedef const __attribute__((address_space(3))) typename M::frag lfrag;
+  const lds_t* orow = lds + (row * LDP + M::KPL * half) * (int)sizeof(T);
+  const lds_t* grow = orow + TILE;
+  float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      typename M::frag a, g;
-      __builtin_memcpy(&a, orow + ks * M::KSTEP, sizeof(a));
-      __builtin_memcpy(&g, grow + ks * M::KSTEP, sizeof(g));
-      part = frag_dot(a, g, part);
-    }
-    const float other = __shfl_xor(part, 1, 2);
-    if (half == 0) Dv[row] = part + other;
+  for (int ks = 0; ks < KS; ++ks) {
+    const typename M::frag a = *reinterpret_cast<lfrag*>(orow + ks * M::KSTEP * (int)sizeof(T));
+    const typename M::frag g = *reinterpret_cast<lfrag*>(grow + ks * M::KSTEP * (int)sizeof(T));
+    part = frag_dot(a, g, part);
   }
+  const float other = __shfl_xor(part, 1, 2);
+  if (half == 0 && row < nr) Dv[r0 + row] = part + other;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -813,8 +835,7 @@ static bool bwd_two_groups(int dtype, const Problem& p) {
 template <typename T, int D>
 static hipError_t launch_rowdot_t(const Problem& p, const void* O, const void* dO, float* Dv, hipStream_t s) {
   const int rows = p.B * p.H * p.N;
-  int grid = (rows + 127) / 128;  // 128 rows per 256-thread block
-  if (grid > 256 * 16) grid = 256 * 16;
+  const int grid = (rows + kRowdotRows - 1) / kRowdotRows;
   hipLaunchKernelGGL((rowdot_kernel<T, D>), dim3(grid), dim3(256), 0, s, (const T*)O, (const T*)dO, Dv, rows);
   return hipGetLastError();
 }
