@@ -429,10 +429,10 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   }
   const int grid = BH * TQ;
   if constexpr (sizeof(T) == 2 && BK == 64) {
-    if (!p.bmask && fwd_two_groups(p, BH * TQ)) {
+    if (!p.bmask && fwd_two_groups(p, (long)BH * ((p.N + 127) / 128))) {
       // Up to d = 64 two such workgroups fit a CU: 64-query workgroups then spread the heaviest
       // query tiles over twice as many CUs.
-      constexpr int NW2 = D <= 64 ? 2 : NW;
+      constexpr int NW2 = D <= 64 ? 2 : 4;
       const int grid2 = BH * ((p.N + 32 * NW2 - 1) / (32 * NW2));
       hipLaunchKernelGGL((fwd_kernel<T, D, NW2, BK, D <= 64 ? 2 : 1, false, false, 2>), dim3(grid2),
                          dim3(2 * NW2 * 64), 0, stream, (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H,
@@ -489,7 +489,10 @@ hipError_t launch_fwd(int dtype, const Problem& p, const void* Q, const void* K,
       case 32: return launch_fwd_t<__bf16, 32, 4, 64, 4>(p, Q, K, V, O, L, s, ns, part);
       case 64: return launch_fwd_t<__bf16, 64, 4, 64, 4>(p, Q, K, V, O, L, s, ns, part);
       case 80: return launch_fwd_t<__bf16, 80, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
-      case 128: return launch_fwd_t<__bf16, 128, 4, 64, 2>(p, Q, K, V, O, L, s, ns, part);
+      // d = 128: 8-wave workgroups (256 queries) share one K/V stream, which halves the K/V reads
+      // beyond L2 per query; register use allows 2 waves per SIMD either way.  Measured on the
+      // B=1 H=36 N=16384 workload: 2546 -> 2472 us (at d = 80 the same change was slower).
+      case 128: return launch_fwd_t<__bf16, 128, 8, 64, 1>(p, Q, K, V, O, L, s, ns, part);
     }
   } else if (dtype == kF32) {
     switch (p.d) {
