@@ -1080,6 +1080,9 @@ hipError_t launch_dkdv(int dtype, const Problem& p, const void* Q, const void* K
   return hipErrorInvalidValue;
 }
 
+// dQ tiles: 4 waves x 32 queries with 32-key tiles up to d = 80 (64-key tiles measured slower there);
+// at d = 128, 8 waves (256 queries) share each 64-key K/V tile, which halves the K/V reads beyond L2
+// per query at the same two waves per SIMD (B=1 H=36 N=16384: 3447 -> 3397 us in a same-box A/B).
 hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                      const void* O, const float* L, float* Dv, void* dQ, hipStream_t s, void* workspace,
                      size_t workspace_bytes) {
@@ -1090,7 +1093,7 @@ hipError_t launch_dq(int dtype, const Problem& p, const void* Q, const void* K, 
   if (dtype == DT && p.d == DD) {                                                                  \
     if constexpr (DT == kF32) return launch_dq_t<T, DD, 4, 32, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part); \
     else if constexpr (DD <= 80) return launch_dq_t<T, DD, 4, 32, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part); \
-    else return launch_dq_t<T, DD, 4, 64, 2>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part);            \
+    else return launch_dq_t<T, DD, 8, 64, 1>(p, Q, K, V, dO, O, L, Dv, dQ, s, ns, part);            \
   }
   ATTN_BWD_CASES(X)
 #undef X
