@@ -235,25 +235,56 @@ __device__ __forceinline__ void dkdv_body(
     }
     auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, qt_hi, SHIFT) : t + 1; };
     if constexpr (DSELF) {
+      static_assert(sizeof(T) == 2, "D rows computed in the dK/dV body: bf16 only");
       // The first stage's loads, the D row loads and the K/V fragments are all in flight before
       // the first wait, so this prologue costs one memory latency rather than three.
       if (cur < qt_hi) load_stage(cur);
-      for (int r = qt0 * BQS + threadIdx.x; r < N; r += NT) {
-        const T* orow = Oin + base + (size_t)r * D;
-        const T* grow = dO + base + (size_t)r * D;
-        float part[2];
+      // D for rows [qt0 BQS, N): LPR lanes per row, lane j loading 16-byte chunk j of the O and dO
+      // rows, so consecutive lanes read consecutive addresses and one load instruction covers whole
+      // rows (one thread per row touched a different memory line in every lane).  The sum keeps the
+      // fragment order of the dQ kernel and the D pass -- chunk j belongs to half j % 2, each half
+      // runs over its chunks in increasing order -- by handing the running sum from lane j - 2 to
+      // lane j, so D agrees with theirs bitwise.
+      constexpr int C = D * (int)sizeof(T) / 16;                        // 16-byte chunks per row
+      constexpr int LPR = C <= 2 ? 2 : C <= 4 ? 4 : C <= 8 ? 8 : 16;  // lanes per row (within a DPP row)
+      constexpr int RPP = NT / LPR;                                    // rows per pass
+      constexpr int U = 4;                                             // passes in flight
+      const int j = (int)threadIdx.x % LPR;
+      const int r0 = qt0 * BQS;
+      const auto rO = make_rsrc(Oin + base, tbytes);
+      for (int p0 = r0; p0 < N; p0 += U * RPP) {
+        u32x4 a[U], g[U];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          part[h] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            typename M::frag a, g;
-            __builtin_memcpy(&a, orow + ks * M::KSTEP + M::KPL * h, sizeof(a));
-            __builtin_memcpy(&g, grow + ks * M::KSTEP + M::KPL * h, sizeof(g));
-            part[h] = frag_dot(a, g, part[h]);
+        for (int u = 0; u < U; ++u) {
+          if (p0 + u * RPP < N) {  // uniform: passes with no row are skipped
+            const int row = p0 + u * RPP + (int)threadIdx.x / LPR;
+            const uint32_t off = (uint32_t)(row * D * (int)sizeof(T) + j * 16);
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            const bool ok = j < C && row < N;
+            a[u] = ok ? buffer_load16(rO, off) : zero;
+            g[u] = ok ? buffer_load16(ro, off) : zero;
           }
         }
-        dself[r - qt0 * BQS] = -(part[0] + part[1]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (p0 + u * RPP < N) {
+            typename M::frag fa, fg;
+            __builtin_memcpy(&fa, &a[u], 16);
+            __builtin_memcpy(&fg, &g[u], 16);
+            float acc = frag_dot(fa, fg, 0.f);
+#pragma unroll
+            for (int st = 1; st < C / 2; ++st) {
+              // lane j takes the running sum of lane j - 2 (DPP row_shr:2; rows of 16 lanes hold whole
+              // groups of LPR lanes), lanes 0 and 1 of a group start from zero
+              const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x112, 0xf, 0xf, true));
+              acc = frag_dot(fa, fg, j >= 2 ? prev : 0.f);
+            }
+            // lane C - 2 adds the other half's sum from lane C - 1 (DPP row_shl:1)
+            const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x101, 0xf, 0xf, true));
+            const int row = p0 + u * RPP + (int)threadIdx.x / LPR;
+            if (j == C - 2 && row < N) dself[row - r0] = -(acc + other);
+          }
+        }
       }
       settle_kv();
       if (cur < qt_hi) store_stage(lds);
