@@ -400,18 +400,21 @@ __device__ __forceinline__ void dkdv_body(
   if constexpr (G == 2) {
     // Group 1 hands its dK, dV sums to the wave of group 0 that owns the same keys (every wave of
     // the workgroup gets here; the stages are no longer read once the loop's last barrier passed).
-    constexpr int F = 2 * KB * NDB * 16;  // floats per lane
-    static_assert(NW * 64 * F * 4 <= 2 * STAGE, "merge buffer fits in the stages");
-    float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
+    // 16 bytes per lane per access, consecutive lanes at consecutive addresses (conflict-free).
+    constexpr int F4 = 2 * KB * NDB * 4;  // float4s per lane
+    static_assert(NW * 64 * F4 * 16 <= 2 * STAGE, "merge buffer fits in the stages");
+    f32x4* mrg = reinterpret_cast<f32x4*>(smem) + w * F4 * 64 + l;
     if (grp == 1) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            mrg[((kb * NDB + i) * 32 + e) * 64] = dk[kb][i][e];
-            mrg[((kb * NDB + i) * 32 + 16 + e) * 64] = dv[kb][i][e];
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 k4 = {dk[kb][i][4 * m], dk[kb][i][4 * m + 1], dk[kb][i][4 * m + 2], dk[kb][i][4 * m + 3]};
+            const f32x4 v4 = {dv[kb][i][4 * m], dv[kb][i][4 * m + 1], dv[kb][i][4 * m + 2], dv[kb][i][4 * m + 3]};
+            mrg[((kb * NDB + i) * 8 + m) * 64] = k4;
+            mrg[((kb * NDB + i) * 8 + 4 + m) * 64] = v4;
           }
     }
     __syncthreads();
@@ -421,9 +424,14 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          dk[kb][i][e] += mrg[((kb * NDB + i) * 32 + e) * 64];
-          dv[kb][i][e] += mrg[((kb * NDB + i) * 32 + 16 + e) * 64];
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 k4 = mrg[((kb * NDB + i) * 8 + m) * 64];
+          const f32x4 v4 = mrg[((kb * NDB + i) * 8 + 4 + m) * 64];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dk[kb][i][4 * m + r] += k4[r];
+            dv[kb][i][4 * m + r] += v4[r];
+          }
         }
   }
 
@@ -516,7 +524,16 @@ constexpr int dq_lds_bytes() {
 // With G = 2 the workgroup has two groups of NW waves over the same queries and key tiles of 2 BK
 // keys: group g takes keys [g BK, (g + 1) BK) of every tile, halving each wave's chain; group 1's
 // dQ sums are added to group 0's through LDS at the end (as in the forward and dK/dV bodies).
-template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false, int G = 1>
+// With STQ the workgroup's rows of Q, dO and O are first copied into LDS after the key stages
+// (dq_stq_bytes more bytes) with contiguous 16-byte loads, and each wave reads its operand
+// fragments from there: the fragment layout read straight from memory touches 32 rows per load
+// instruction, and with G = 2 both groups read the same rows.  Values and reduction order are the
+// same either way.
+template <typename T, int D, int NW>
+constexpr int dq_stq_bytes() {
+  return 3 * 32 * NW * lds_pitch<T, (D + 31) / 32 * 32>() * (int)sizeof(T);
+}
+template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false, int G = 1, bool STQ = false>
 __device__ __forceinline__ void dq_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
@@ -540,6 +557,7 @@ __device__ __forceinline__ void dq_body(
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
   static_assert(G == 1 || (G == 2 && !BSP && !SPLIT), "two key groups: dense and unsplit only");
+  static_assert(!STQ || !BSP, "staged query rows: dense masks only");
 
   lds_t* lds = (lds_t*)smem;
   lds_t* map = lds + 4 * TILE;
@@ -584,12 +602,23 @@ __device__ __forceinline__ void dq_body(
   const auto rv = make_rsrc(V + base, (uint32_t)(kend * D * sizeof(T)));
 
   typename M::frag qf[KS], of[KS];
+  if constexpr (!STQ) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
-    of[ks] = frag_global<T>(ro, q, D, ks * M::KSTEP);
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
+      of[ks] = frag_global<T>(ro, q, D, ks * M::KSTEP);
+    }
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : 0.f;
+  // STQ: rows q0 .. q0 + QT - 1 of Q, dO, O (rows past N read as zero, as the fragments would).
+  constexpr int QTILE = QT * LD * (int)sizeof(T);
+  lds_t* qs = lds + 4 * TILE;
+  TileCopy<T, STQ ? QT : 1, STQ ? D : 16 / (int)sizeof(T), LD, NT> qcp, ocp, ocp2;
+  if constexpr (STQ) {
+    qcp.load(rq, q0);
+    ocp.load(ro, q0);
+    if (Oin) ocp2.load(make_rsrc(Oin + base, tbytes), q0);
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -614,12 +643,27 @@ __device__ __forceinline__ void dq_body(
     kc.load(rk, cur * BKT);
     vc.load(rv, cur * BKT);
   }
+  if constexpr (STQ) {
+    qcp.store(qs);
+    ocp.store(qs + QTILE);
+    if (Oin) ocp2.store(qs + 2 * QTILE);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = M::frag_direct(qs, LD, 32 * w * LD + ks * M::KSTEP);
+      of[ks] = M::frag_direct(qs + QTILE, LD, 32 * w * LD + ks * M::KSTEP);
+    }
+  }
   float dq_;
   if (Oin) {
     const auto rO = make_rsrc(Oin + base, tbytes);
     float dpart = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) dpart = frag_dot(frag_global<T>(rO, q, D, ks * M::KSTEP), of[ks], dpart);
+    for (int ks = 0; ks < KS; ++ks) {
+      const typename M::frag oa = STQ ? M::frag_direct(qs + 2 * QTILE, LD, 32 * w * LD + ks * M::KSTEP)
+                                      : frag_global<T>(rO, q, D, ks * M::KSTEP);
+      dpart = frag_dot(oa, of[ks], dpart);
+    }
     dq_ = dpart + swap_halves(dpart);
     if (half == 0 && q < N && split == 0 && grp == 0) Dv[(size_t)bh * N + q] = dq_;
   } else {
@@ -695,21 +739,29 @@ __device__ __forceinline__ void dq_body(
   if constexpr (G == 2) {
     // Group 1 hands its dQ sums to the wave of group 0 that owns the same queries (the tiles are
     // no longer read: the loop ended on a barrier and staged nothing after it).
-    constexpr int F = NDB * 16;  // floats per lane
-    static_assert(NW * 64 * F * 4 <= 4 * TILE, "merge buffer fits in the tile stages");
-    float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
+    // 16 bytes per lane per access, consecutive lanes at consecutive addresses (conflict-free).
+    constexpr int F4 = NDB * 4;  // float4s per lane
+    static_assert(NW * 64 * F4 * 16 <= 4 * TILE, "merge buffer fits in the tile stages");
+    f32x4* mrg = reinterpret_cast<f32x4*>(smem) + w * F4 * 64 + l;
     if (grp == 1) {
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mrg[(16 * i + e) * 64] = acc[i][e];
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 a4 = {acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
+          mrg[(4 * i + m) * 64] = a4;
+        }
     }
     __syncthreads();
     if (grp == 1) return;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][e] += mrg[(16 * i + e) * 64];
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 a4 = mrg[(4 * i + m) * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][4 * m + r] += a4[r];
+      }
   }
 
   if constexpr (SPLIT) {
@@ -835,8 +887,11 @@ __global__ __launch_bounds__(512, 1) void bwd_small2_kernel(
     const T* __restrict__ O, const float* __restrict__ Lse, float* __restrict__ Dv, T* __restrict__ dQ,
     T* __restrict__ dK, T* __restrict__ dV, int BH, int H, int N, int causal, float scale, float scale_log2,
     const int32_t* __restrict__ kv_len, SmallOrder order) {
+  // dQ items stage their query rows in LDS (STQ) where that fits in the dK/dV items' allocation.
+  constexpr bool STQ = D <= 64;
   __shared__ __attribute__((aligned(16))) char
-      smem[cmax(dq_lds_bytes<T, D, 64, false>(), dkdv_lds_bytes<T, D, 4, 64, true, false, 1, false, 2>())];
+      smem[cmax(dq_lds_bytes<T, D, 64, false>() + (STQ ? dq_stq_bytes<T, D, 4>() : 0),
+                dkdv_lds_bytes<T, D, 4, 64, true, false, 1, false, 2>())];
   const int c = order.cls[blockIdx.x / BH];
   // Block of the bodies' rank-major grids: rank (c & 0x7f) of head blockIdx.x % BH.
   const int b = (c & 0x7f) * BH + (int)blockIdx.x % BH;
@@ -845,8 +900,8 @@ __global__ __launch_bounds__(512, 1) void bwd_small2_kernel(
         smem, b, Q, K, V, dO, O, Lse, Dv, dK, dV, BH, H, N, causal,
         scale, scale_log2, kv_len, nullptr);
   else
-    dq_body<T, D, 4, 32, false, false, 2>(smem, b, Q, K, V, dO, O, Lse, Dv,
-                                          dQ, BH, H, N, causal, scale, scale_log2, kv_len, nullptr);
+    dq_body<T, D, 4, 32, false, false, 2, STQ>(smem, b, Q, K, V, dO, O, Lse, Dv,
+                                               dQ, BH, H, N, causal, scale, scale_log2, kv_len, nullptr);
 }
 
 // ------------------------------------------------------------------------------------------
