@@ -122,6 +122,9 @@ __device__ __forceinline__ void dkdv_body(
   constexpr int STAGE = 2 * TILE + 2 * BQS * (int)sizeof(float);  // Q tile, dO tile, L row, D row
   constexpr int SHIFT = BQ == 64 ? 0 : 1;                         // query tiles per mask block = 1 << SHIFT
   static_assert(2 * BQS <= NT, "one thread per staged L / D value");
+  // K and V rows staged through the second stage (see kst below): the D-computing bodies of two-group
+  // workgroups, whose stage tiles hold exactly the workgroup's KT keys.
+  constexpr bool STK = DSELF && G == 2 && KB == 1 && !VLDS && !BSP && BQS == 32 * NW && sizeof(T) == 2;
   static_assert(G == 1 || (G == 2 && !BSP && !SPLIT), "two query groups: dense and unsplit only");
   static_assert(!BSP || ((BQ == 32 || BQ == 64) && KT % kMaskBlock == 0 && KT / kMaskBlock <= 8),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
@@ -171,21 +174,40 @@ __device__ __forceinline__ void dkdv_body(
       vcp.load(rv, k0);
       vcp.store(vt);
     }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kf[kb][ks] = frag_global<T>(rk, kw + 32 * kb + col, D, ks * M::KSTEP);
-        if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
-      }
-    auto settle_kv = [&]() {
+    // STK: the workgroup's K and V rows are copied with contiguous loads into the second stage's
+    // Q and dO slots (free until the first stage is consumed), and the fragments read from there.
+    TileCopy<T, STK ? KT : 1, STK ? D : 16 / (int)sizeof(T), LD, NT> kst, vst;
+    if constexpr (STK) {
+      kst.load(rk, k0);
+      vst.load(rv, k0);
+    } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          settle(kf[kb][ks]);
-          if constexpr (!VLDS) settle(vf[kb][ks]);
+          kf[kb][ks] = frag_global<T>(rk, kw + 32 * kb + col, D, ks * M::KSTEP);
+          if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
         }
+    }
+    auto settle_kv = [&]() {
+      if constexpr (STK) {
+        kst.store(lds + STAGE);
+        vst.store(lds + STAGE + TILE);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[0][ks] = M::frag_direct(lds + STAGE, LD, KW * w * LD + ks * M::KSTEP);
+          vf[0][ks] = M::frag_direct(lds + STAGE + TILE, LD, KW * w * LD + ks * M::KSTEP);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            settle(kf[kb][ks]);
+            if constexpr (!VLDS) settle(vf[kb][ks]);
+          }
+      }
     };
     // Without DSELF the fragments are waited for here (keeping them out of the first stage's
     // register peak); with DSELF only after the D rows, whose loads then overlap theirs.
