@@ -106,9 +106,20 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   const auto rk = make_rsrc(K + base, (uint32_t)(kend * D * sizeof(T)));  // keys >= kend read as 0
   const auto rv = make_rsrc(V + base, (uint32_t)(kend * D * sizeof(T)));
 
+  // With two key groups both groups need the same Q fragments: the workgroup's Q rows are then
+  // copied with contiguous loads into the second stage's K slot (free until the first iteration
+  // refills it) and the fragments read from there, rather than each group reading them in fragment
+  // layout from memory (16 bytes from each of 32 rows per load instruction).
+  constexpr bool STQ = G == 2;
   typename M::frag qf[KS];
+  TileCopy<T, STQ ? QT : 1, STQ ? D : 16 / (int)sizeof(T), LD, NT> qst;
+  if constexpr (STQ) {
+    static_assert(QT <= BKT, "Q rows fit in a K slot");
+    qst.load(rq, q0);
+  } else {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
+  }
 
   f32x16 o[NDB];
 #pragma unroll
@@ -134,15 +145,24 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     kc.load(rk, cur * BKT);
     vc.load(rv, cur * BKT);
   }
-  // The Q fragments were requested first: waiting for them here leaves the first K/V tile's loads
-  // in flight, so the two memory latencies overlap.
+  // The Q fragments (or rows) were requested first: waiting for them here leaves the first K/V
+  // tile's loads in flight, so the two memory latencies overlap.
+  if constexpr (STQ) {
+    qst.store(lds + 2 * TILE);
+  } else {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+  }
   if (cur < t_hi) {
     kc.store(lds);
     vc.store(lds + TILE);
   }
   __syncthreads();
+  if constexpr (STQ) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = M::frag_direct(lds + 2 * TILE, LD, 32 * w * LD + ks * M::KSTEP);
+    __syncthreads();  // every wave holds its fragments before the first iteration refills the slot
+  }
   int nxt = cur < t_hi ? after(cur) : t_hi;
   if (nxt < t_hi) {
     kc.load(rk, nxt * BKT);
