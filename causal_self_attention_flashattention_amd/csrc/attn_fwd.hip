@@ -181,13 +181,13 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
       // Scores of this wave's keys of the tile (raw, unscaled); masked ones replaced (only on
       // tiles that cross the diagonal or the key end).
       f32x16 s[NB];
-      auto scores = [&](const lds_t* kt) {
+      auto scores = [&]() {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           s[nb] = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            s[nb] = M::mma(M::frag_direct(kt, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+            s[nb] = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
         }
         if ((causal && k0 + BK - 1 > qw) || k0 + BK > kv) {
 #pragma unroll
@@ -233,12 +233,12 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
           lsum = M::frag_sum(pf[c], lsum);
         }
       };
-      scores(ktile);
+      scores();
       // Head dims above kSumCheckMaxD, and a wave's first tile, take the tile's row max first.
-      // Otherwise each key block's weights are formed with the running max as it stands: a lane whose weights sum to
-      // at most 2^kRescaleSlack has every weight within that bound, which is all the running max
-      // must guarantee, so the block's max is only taken (and the max moved) when some lane
-      // exceeds it or overflowed -- the scores of that block are then recomputed.
+      // Otherwise each key block's weights are formed with the running max as it stands: a lane
+      // whose weights sum to at most 2^kRescaleSlack has every weight within that bound, which is
+      // all the running max must guarantee, so the block's max is only taken (and the max moved)
+      // when some lane exceeds it or overflowed -- the scores of that block are then recomputed.
       const bool check = !first && D <= kSumCheckMaxD;
       if (first || D > kSumCheckMaxD) {
         move_max(0, NB);
