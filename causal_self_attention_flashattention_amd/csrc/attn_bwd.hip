@@ -719,7 +719,12 @@ __device__ __forceinline__ void dq_body(
       for (int nb = 0; nb < NB; ++nb) {
         const int kb0 = cur * BKT + grp * BK + nb * 32;
         if (kb0 >= kend || (causal && kb0 > qw_last)) continue;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // At d = 128 the dP^T accumulators start at -D of this lane's query, so they end as dP - D
+        // (eq. 17's bracket) with no subtraction per score (2% faster there; at d <= 80 the extra
+        // live registers cost more than the subtraction).
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[e] = D > 80 ? -dq_ : 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           s = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s);
@@ -732,7 +737,7 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
-          dp[e] = p * (dp[e] - dq_);
+          dp[e] = D > 80 ? p * dp[e] : p * (dp[e] - dq_);
         }
 #pragma unroll
         for (int c = 0; c < M::CALLS32; ++c) {
