@@ -14,6 +14,12 @@ Algorithmic FLOPs (matrix products only, 2 FLOPs per multiply-add; causal-skippe
 dQ kernel's recompute of S and dP not counted):
   npairs = sum_i (number of unmasked keys of query i)
   forward 4*d*npairs per head (Q K^T and P V), backward 10*d*npairs per head (S, dP, dV, dK, dQ).
+
+The headline workload is the largest model shape, B=1 H=36 N=16384 d=128 ("10b-16k"); the
+d = 64 long-context shape B=4 H=20 N=4096 ("large-4k") is timed in the same run and reported under
+"secondary" with the same fields.  Per-step device times (HIP events between consecutive steps)
+give the mean, standard deviation and median; `value` itself is wall-clock throughput over the
+K timed steps between two synchronisations.
 """
 
 from __future__ import annotations
@@ -34,7 +40,8 @@ METRIC = "causal attention fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-DEFAULT_WORKLOAD = "gpt2-small"
+DEFAULT_WORKLOAD = "10b-16k"
+SECONDARY_WORKLOADS = ("large-4k",)
 KERNELS_SPLIT = ("fwd", "dq", "dkdv")  # launch order of one step when attn_bwd launches two kernels
 KERNELS_FUSED = ("fwd", "bwd")        # ... and when its dQ and dK/dV work share one launch
 KERNEL_SOURCES = ("attn_device.h", "attn_fwd.hip", "attn_bwd.hip")
@@ -85,13 +92,16 @@ def load_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(inputs, w, kv_list, target_s: float):
-    """Time the float64 oracle (as it stands) on a bounded sample of heads of the same workload."""
+    """Time the float64 oracle (as it stands) on a bounded sample of heads of the same workload:
+    whole heads, forward then backward, until ``target_s`` has passed (at least one head)."""
     import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
 
     import oracle.attention as O
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    vendor = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer')})" for p in blas)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done, flops = 0, 0
     t0 = time.perf_counter()
@@ -111,8 +121,10 @@ def cpu_baseline(inputs, w, kv_list, target_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "blas": vendor or "unknown",
         "sample": f"{done} (batch, head) fwd+bwd passes of the {w.name} workload "
-                  f"({done / len(heads):.2f} x its {len(heads)} heads), float64 numpy, {el:.1f} s",
+                  f"({done / len(heads):.3f} x its {len(heads)} heads: whole heads, materialised N x N, "
+                  f"float64 numpy), {el:.1f} s, scaled by the same algorithmic FLOP count",
     }
 
 
@@ -164,42 +176,14 @@ def rowdot_bench(args, w, lib, P_, B, H, N, d, dt, stream, step_binding):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="record the per-kernel HIP events on every n-th timed step (1 = every step)")
-    ap.add_argument("--rowdot", action="store_true",
-                    help="instead of the attention step, time the stand-alone D = rowsum(O o dO) pass "
-                         "(attn_bwd_rowdot) on the workload's O and dO and report HBM GB/s")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="instead of the attention step, time a plain device-to-device copy of this many bytes "
-                         "(the reference kernel that HBM byte counters are scaled against)")
-    args = ap.parse_args()
+def time_workload(args, name, attn, lib, hip, torch):
+    """Run W warm-up and K timed steps of one workload; return its JSON record (without cpu_baseline)
+    and its CPU inputs."""
+    import statistics
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): attention is independent "
-              "per (batch, head), so more GPUs would only split heads; no multi-GPU run is provided.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    if args.copy_bytes > 0:
-        copy_probe(args.copy_bytes, args.steps)
-        return
-
-    import causal_self_attention_flashattention_amd as attn
     from causal_self_attention_flashattention_amd.inputs import WORKLOADS, make_workload_inputs
 
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[name]
     inputs = make_workload_inputs(w, args.seed)
     kv_list = None if inputs["kv_len"] is None else inputs["kv_len"].tolist()
     kv = w.N if kv_list is None else kv_list[0]
@@ -210,14 +194,10 @@ def main():
     o, L = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     D = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    attn.load_library()
 
     # The timed loop calls the C ABI directly with pre-resolved pointers and records the HIP events
     # through the runtime, so that host-side overhead stays well below the kernels' own time (the
     # arguments were validated by the same calls through the binding during warm-up).
-    lib = attn.load_library()
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded (same soname)
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     P_ = {n: t.data_ptr() for n, t in dict(q=q, k=k, v=v, o=o, L=L, do=do, D=D, dq=dq, dk=dk, dv=dv).items()}
     kvp = None if kvd is None else kvd.data_ptr()
@@ -230,13 +210,13 @@ def main():
 
     if args.rowdot:
         rowdot_bench(args, w, lib, P_, B, H, N, d, dt, stream, step_binding)
-        return
+        return None, None
 
     fused = attn.bwd_launches(B, H, N, d, q.dtype) == 1
     KERNELS = KERNELS_FUSED if fused else KERNELS_SPLIT
+    rec = hip.hipEventRecord
 
     def step(ev=None):
-        rec = hip.hipEventRecord
         if ev is not None:
             rec(ev[0], stream)
         st = lib.attn_fwd(P_["q"], P_["k"], P_["v"], P_["o"], P_["L"], B, H, N, d, c, sc, dt, kvp, stream)
@@ -267,20 +247,30 @@ def main():
     every = max(1, args.event_every)
     n_ev = (args.steps + every - 1) // every
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(n_ev)]
-    for e in evs:  # materialise the events before the timed region
+    # one event before every timed step and one after the last: per-step device times
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in evs + [sev]:  # materialise the events before the timed region
         for x in e:
             x.record()
     torch.cuda.synchronize()
     hev = [[ctypes.c_void_p(x.cuda_event) for x in e] for e in evs]
+    hsev = [ctypes.c_void_p(x.cuda_event) for x in sev]
     t0 = time.perf_counter()
+    per_step = not args.no_step_events
     for i in range(args.steps):
+        if per_step:
+            rec(hsev[i], stream)
         step(hev[i // every] if i % every == 0 else None)
+    if per_step:
+        rec(hsev[args.steps], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    per_kernel_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n_ev
-                     for j, name in enumerate(KERNELS)}
+    per_kernel_ms = {kn: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n_ev for j, kn in enumerate(KERNELS)}
     event_ms_per_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / n_ev
+    # without per-step events, the event-bracketed steps stand in for the distribution
+    step_ms = ([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)] if per_step
+               else [e[0].elapsed_time(e[-1]) for e in evs])
 
     work = kernel_work(w, kv)
     P = npairs(w.N, kv, w.causal)
@@ -315,6 +305,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms": {"mean": statistics.fmean(step_ms),
+                    "std": statistics.stdev(step_ms) if len(step_ms) > 1 else 0.0,
+                    "median": statistics.median(step_ms), "min": min(step_ms), "max": max(step_ms),
+                    "source": "HIP events between consecutive timed steps" if per_step
+                    else "HIP events around every --event-every-th timed step"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -322,12 +317,70 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "kv_len": kv, "seed": w.seed if args.seed is None else args.seed,
-                   "pct_of_peak": 100.0 * value / peak, "peak_tflops": peak,
+                   "flop_per_step": total_flop, "pct_of_peak": 100.0 * value / peak, "peak_tflops": peak,
                    "event_ms_per_step": event_ms_per_step, "event_steps": n_ev, "kernels": kernels},
         "roofline": roof,
     }
+    return out, (inputs, w, kv_list)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--secondary", default=",".join(SECONDARY_WORKLOADS),
+                    help="comma-separated workloads timed after the headline one and reported under "
+                         "'secondary' (empty: none)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record the per-kernel HIP events on every n-th timed step (1 = every step)")
+    ap.add_argument("--no-step-events", action="store_true",
+                    help="record no HIP event between consecutive steps (for launch-bound workloads, where an "
+                         "event record adds a few microseconds to each step)")
+    ap.add_argument("--rowdot", action="store_true",
+                    help="instead of the attention step, time the stand-alone D = rowsum(O o dO) pass "
+                         "(attn_bwd_rowdot) on the workload's O and dO and report HBM GB/s")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the attention step, time a plain device-to-device copy of this many bytes "
+                         "(the reference kernel that HBM byte counters are scaled against)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): attention is independent "
+              "per (batch, head), so more GPUs would only split heads; no multi-GPU run is provided.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_bytes > 0:
+        copy_probe(args.copy_bytes, args.steps)
+        return
+
+    import causal_self_attention_flashattention_amd as attn
+
+    lib = attn.load_library()
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded (same soname)
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    out, ctx = time_workload(args, args.workload, attn, lib, hip, torch)
+    if out is None:  # --rowdot printed its own line
+        return
+    if not args.rowdot:
+        sec = {}
+        for name in [n for n in args.secondary.split(",") if n and n != args.workload]:
+            r, _ = time_workload(args, name, attn, lib, hip, torch)
+            sec[name] = {key: r[key] for key in ("value", "ms_per_step", "step_ms", "config", "roofline")}
+            torch.cuda.empty_cache()
+        if sec:
+            out["secondary"] = sec
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inputs, w, kv_list, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(*ctx, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

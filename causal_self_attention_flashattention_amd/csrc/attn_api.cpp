@@ -33,6 +33,9 @@ int check_common(int B, int H, int N, int d, int dtype, float scale, bool need_s
   if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_E_SHAPE;
   const int64_t elems = (int64_t)B * H * N * d;
   if (elems >= ((int64_t)1 << 31)) return ATTN_E_SHAPE;
+  // The kernels address one head of a tensor through a 32-bit buffer resource with signed 32-bit
+  // byte offsets, so a head (N * d elements) must span fewer than 2^31 bytes.
+  if ((int64_t)N * d * (int64_t)elem_size(dtype) >= ((int64_t)1 << 31)) return ATTN_E_SHAPE;
   if (!attn::fwd_supported(dtype, d)) return ATTN_E_HEADDIM;
   // The kernels take row maxima of the unscaled scores and mask before scaling, both of which
   // assume scale > 0.
@@ -73,7 +76,7 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "B, H, N and d must be >= 1 and B*H*N*d < 2^31";
+    case ATTN_E_SHAPE: return "B, H, N and d must be >= 1, B*H*N*d < 2^31 and one head (N*d elements) < 2^31 bytes";
     case ATTN_E_HEADDIM: return "unsupported head dim (supported: 16, 32, 64, 80, 128)";
     case ATTN_E_DTYPE: return "unknown dtype (0 = float32, 1 = bfloat16)";
     case ATTN_E_ALIGN: return "a pointer is not 16-byte aligned";

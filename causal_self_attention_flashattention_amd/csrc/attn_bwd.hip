@@ -1,6 +1,6 @@
 // Attention backward with recomputation (gfx950): three kernels on one stream.
 //
-// The math is eqs. (13)-(19) of the CS336 Assignment 2 (systems) handout, §4.1 ("backward
+// The math is eqs. (13)-(19) of the CS336 Assignment 2 (systems) handout, §4.2.2 ("backward
 // pass with recomputation"): S = scale Q K^T, P_ij = exp(S_ij - L_i), dV = P^T dO,
 // dP = dO V^T, dS_ij = P_ij (dP_ij - D_i), dQ = scale dS K, dK = scale dS^T Q, with
 // D = rowsum(O o dO) computed first.  Following the key idea of the handout's tiled backward
@@ -308,6 +308,10 @@ __device__ __forceinline__ void dkdv_body(
           }
         }
       }
+      // Rows [N, N rounded up to a stage) of the last stage are read as the dP accumulators'
+      // starting value too; their scores are masked (weight 0), but 0 times a non-finite leftover
+      // of this LDS would still be NaN, so they start at 0.
+      for (int row = N + (int)threadIdx.x; row < (N + BQS - 1) / BQS * BQS; row += NT) dself[row - r0] = 0.f;
       settle_kv();
       if (cur < qt_hi) store_stage(lds);
     } else if (cur < qt_hi) {

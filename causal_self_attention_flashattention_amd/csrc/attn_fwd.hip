@@ -2,7 +2,7 @@
 //
 // Computes, per (batch, head), O = softmax(mask(scale * Q K^T)) V and the row logsumexp
 // L_i = log sum_j exp(S_ij) of the scaled, masked scores (natural log), following Algorithm 1
-// ("FlashAttention-2 forward pass") of the CS336 Assignment 2 (systems) handout, §4.1, with
+// ("FlashAttention-2 forward pass") of the CS336 Assignment 2 (systems) handout, §4.2.2, with
 // the causal mask of its Problem (flash_forward)(c) and an optional per-batch key length.
 //
 // Work decomposition: one workgroup per (head, tile of 32*NW queries); wave w owns 32 queries.

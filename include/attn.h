@@ -1,8 +1,8 @@
 /* attn.h -- C ABI of libattn: tiled causal / key-padded self-attention, forward and backward,
  * for AMD Instinct MI355X (gfx950).
  *
- * What is computed (notation of the CS336 Assignment 2 (systems) handout, §4.1 "Optimizing
- * Attention with FlashAttention-2"):
+ * What is computed (notation of the CS336 Assignment 2 (systems) handout: eq. 1 in §4.1 "Optimizing
+ * Attention with FlashAttention-2", everything else in §4.2.2 "FlashAttention-2 forward pass"):
  *   forward  (eq. 1, eqs. 4-6, eq. 12, Algorithm 1):
  *     S = scale * Q K^T, masked entries removed, P = row softmax(S), O = P V,
  *     L_i = log sum_j exp(S_ij) over the unmasked entries of row i (natural log).
@@ -42,7 +42,8 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
 typedef enum {
   ATTN_OK = 0,
   ATTN_E_NULL = -1,    /* a required pointer is NULL */
-  ATTN_E_SHAPE = -2,   /* B, H, N or d < 1, or B*H*N*d >= 2^31 elements */
+  ATTN_E_SHAPE = -2,   /* B, H, N or d < 1, B*H*N*d >= 2^31 elements, or one head's N*d elements
+                          span 2^31 bytes or more (the kernels' per-head 32-bit buffer offsets) */
   ATTN_E_HEADDIM = -3, /* no kernel for this head dim (supported: 16, 32, 64, 80, 128) */
   ATTN_E_DTYPE = -4,   /* dtype is not an attn_dtype */
   ATTN_E_ALIGN = -5,   /* a pointer is not 16-byte aligned */
@@ -51,7 +52,7 @@ typedef enum {
   ATTN_E_SCALE = -8    /* scale is not a finite number > 0 */
 } attn_status;
 
-/* Forward pass (Algorithm 1 of the handout, §4.1, with the causal flag of Problem
+/* Forward pass (Algorithm 1 of the handout, §4.2.2, with the causal flag of Problem
  * (flash_forward)(c)).
  *   Q, K, V  in : [B,H,N,d] dtype
  *   O        out: [B,H,N,d] dtype, softmax(mask(scale Q K^T)) V
@@ -63,7 +64,7 @@ typedef enum {
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N, int d,
              int causal, float scale, int dtype, const int32_t* kv_len, hipStream_t stream);
 
-/* Backward pass (eqs. 13-19 of the handout, §4.1; the two-kernel split of §4.2.3 that
+/* Backward pass (eqs. 13-19 of the handout, §4.2.2; the two-kernel split of §4.2.3 that
  * recomputes P once for dK/dV and once for dQ).
  *   Q, K, V, O, dO in : [B,H,N,d] dtype (O and L as returned by attn_fwd for the same inputs)
  *   L              in : [B,H,N] float32
@@ -74,13 +75,13 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
              int dtype, const int32_t* kv_len, hipStream_t stream);
 
-/* The backward's first step alone: D_i = sum_c O_ic dO_ic in float32 (handout §4.1, the D
+/* The backward's first step alone: D_i = sum_c O_ic dO_ic in float32 (handout §4.2.2, the D
  * vector of the backward pass with recomputation).  O, dO: [B,H,N,d] dtype; D: [B,H,N] float32. */
 int attn_bwd_rowdot(const void* O, const void* dO, float* D, int B, int H, int N, int d, int dtype,
                     hipStream_t stream);
 
 /* The backward's second step alone: dK and dV for every key tile (eqs. 13-17 and 19 of the
- * handout, §4.1), P recomputed from L, D taken from attn_bwd_rowdot (or from attn_bwd_dq called
+ * handout, §4.2.2), P recomputed from L, D taken from attn_bwd_rowdot (or from attn_bwd_dq called
  * with O).  Arguments as for attn_bwd; D is an input here. */
 int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L, const float* D,
                   void* dK, void* dV, int B, int H, int N, int d, int causal, float scale, int dtype,

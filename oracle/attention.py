@@ -7,10 +7,10 @@ helpers) and never receives a value produced by the GPU path.
 
 What it computes, and where that is defined:
 
-* Forward: eq. (1) and eqs. (4)-(6) of the CS336 Assignment 2 (systems) handout, §4.1
-  "Optimizing Attention with FlashAttention-2": ``S = scale * Q K^T``, masked entries removed,
-  row softmax ``P``, ``O = P V``.  The logsumexp ``L_i = log sum_j exp(S_ij)`` is eq. (12),
-  natural log, over the unmasked entries of row i.
+* Forward: eq. (1) of the CS336 Assignment 2 (systems) handout (§4.1 "Optimizing Attention
+  with FlashAttention-2") and eqs. (4)-(6) of its §4.2.2 "FlashAttention-2 forward pass":
+  ``S = scale * Q K^T``, masked entries removed, row softmax ``P``, ``O = P V``.  The logsumexp
+  ``L_i = log sum_j exp(S_ij)`` is eq. (12), natural log, over the unmasked entries of row i.
 * Masking: Problem (flash_forward)(c) of the same handout builds a square causal mask from
   query and key index vectors and pushes masked scores to a large negative value so they get
   no weight. Here the weight of a masked entry is exactly 0 (``np.where``), which is what the
@@ -183,21 +183,26 @@ def head_rows(q, k, v, do, rows, *, causal: bool, scale: float, kv: int | None =
     return o, lse, dq, dd
 
 
-def head_tail_keys(q, k, v, do, ntail: int, *, scale: float):
-    """dK_j, dV_j (eqs. 7 and 11) for the last ``ntail`` keys of one causal head without padding.
+def head_tail_keys(q, k, v, do, ntail: int, *, scale: float, kv: int | None = None):
+    """dK_j, dV_j (eqs. 7 and 11) for the last ``ntail`` visible keys of one causal head.
 
-    Under the causal mask key j is seen only by queries i >= j, so for the last ntail keys the
-    sums over i run over the last ntail rows alone: dV_j = sum_i P_ij do_i, dK_j = scale sum_i
-    dS_ij q_i, with each row's P_i and dS_i from that row of the definition.
-    Returns ``(dK [ntail, d], dV [ntail, d])`` in float64, keys N - ntail .. N - 1.
+    Under the causal mask key j is seen only by queries i >= j, so for the keys
+    j0 = kv' - ntail .. kv' - 1 (kv' = kv with key padding, else N) the sums over i run over
+    rows j0 .. N - 1 alone: dV_j = sum_i P_ij do_i, dK_j = scale sum_i dS_ij q_i, with each row's
+    P_i and dS_i from that row of the definition.  With padding, the rows past kv still see these
+    keys (queries are never masked), so they are part of the sums.
+    Returns ``(dK [ntail, d], dV [ntail, d])`` in float64, keys kv' - ntail .. kv' - 1.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     n = k.shape[0]
-    j0 = n - ntail
+    hi = n if kv is None else kv
+    if not 1 <= ntail <= hi:
+        raise ValueError("ntail must be in [1, number of visible keys]")
+    j0 = hi - ntail
     dk = np.zeros((ntail, k.shape[1]))
     dv = np.zeros((ntail, v.shape[1]))
     for i in range(j0, n):
-        keys, p, _, ds, _ = _row_terms(q, k, v, do, i, True, scale, None)
+        keys, p, _, ds, _ = _row_terms(q, k, v, do, i, True, scale, kv)
         sel = keys >= j0
         dv[keys[sel] - j0] += p[sel, None] * do[i][None, :]
         dk[keys[sel] - j0] += scale * ds[sel, None] * q[i][None, :]
@@ -253,5 +258,5 @@ def rowsum_p_dp(q, k, v, do, *, causal: bool, scale: float, kv_len=None, heads=N
 
 
 def rowsum_o_do(o, do):
-    """``D = rowsum(O o dO)`` (handout §4.1, "backward pass with recomputation"), float64."""
+    """``D = rowsum(O o dO)`` (handout §4.2.2, "backward pass with recomputation"), float64."""
     return (_f64(o) * _f64(do)).sum(axis=-1)

@@ -82,6 +82,10 @@ def _bwd(lib, **kw):
     (dict(Q=None), E_NULL), (dict(O=None), E_NULL), (dict(L=None), E_NULL),
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(d=0), E_SHAPE),
     (dict(B=1024, H=1024, N=1024, d=64), E_SHAPE),
+    # one head must span < 2^31 bytes (32-bit per-head buffer offsets), even when B*H*N*d < 2^31
+    (dict(N=1 << 22, d=128, dtype=0), E_SHAPE),         # float32 head of exactly 2 GiB
+    (dict(N=(1 << 23) + 64, d=128), E_SHAPE),           # bfloat16 head just over 2 GiB
+    (dict(N=(1 << 24) + 1, d=64), E_SHAPE),             # bfloat16, d = 64
     (dict(d=96), E_HEADDIM), (dict(d=48), E_HEADDIM), (dict(dtype=7), E_DTYPE),
     (dict(scale=float("nan")), E_SCALE), (dict(scale=float("inf")), E_SCALE),
     (dict(scale=0.0), E_SCALE), (dict(scale=-0.125), E_SCALE),
@@ -97,6 +101,7 @@ def test_fwd_rejects_bad_arguments(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(dO=None), E_NULL), (dict(D=None), E_NULL), (dict(dV=None), E_NULL),
     (dict(N=0), E_SHAPE), (dict(d=100), E_HEADDIM), (dict(dtype=-1), E_DTYPE),
+    (dict(N=1 << 22, d=128, dtype=0), E_SHAPE), (dict(N=(1 << 23) + 64, d=128), E_SHAPE),
     (dict(dK=A + 7 * SZ + 2), E_ALIGN),
     (dict(dQ=A), E_ALIAS),                # dQ == Q
     (dict(dK=A + 6 * SZ), E_ALIAS),       # dK == dQ
@@ -112,6 +117,14 @@ def test_rowdot_rejects_bad_arguments(lib):
     assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 16, 24, 1, None) == E_HEADDIM
     assert lib.attn_bwd_rowdot(A, A + SZ, A + 16, 1, 1, 16, 64, 1, None) == E_ALIAS
     assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 16, 64, 3, None) == E_DTYPE
+    assert lib.attn_bwd_rowdot(A, A + SZ, A + 2 * SZ, 1, 1, 1 << 22, 128, 0, None) == E_SHAPE
+
+
+def test_per_head_limit_in_queries(lib):
+    # the planning queries apply the same limit (0 = bad arguments / no kernel)
+    assert lib.attn_fwd_workspace_bytes(1, 1, 1 << 22, 128, 0) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, (1 << 23) + 64, 128, 1) == 0
+    assert lib.attn_bwd_launches(1, 1, 1 << 22, 128, 0) == E_SHAPE
 
 
 def _dq(lib, **kw):

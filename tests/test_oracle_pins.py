@@ -141,7 +141,7 @@ def pin_causality(impl):
 
 
 def pin_d_identity(impl):
-    """Handout §4.1: rowsum(P o dP) = rowsum(O o dO), since P dP^T = O dO^T."""
+    """Handout §4.2.2: rowsum(P o dP) = rowsum(O o dO), since P dP^T = O dO^T."""
     r = _rng(8)
     n, d = 31, 9
     q, k, v, do = r.normal(size=(4, n, d))
@@ -406,7 +406,21 @@ def rpin_tail_keys_match_full(impl):
         np.testing.assert_allclose(tv, dv[n - nt:], atol=1e-13)
 
 
-RPINS = [rpin_rows_match_full, rpin_rows_zero_query, rpin_tail_keys_match_full]
+def rpin_tail_keys_padded_match_full(impl):
+    """With key padding kv < N, the last visible keys' dK, dV (from rows j0 .. N - 1, the rows past kv
+    included) equal the materialised backward; keys past kv have no gradient at all."""
+    r = _rng(24)
+    n, d = 41, 5
+    q, k, v, do = r.normal(size=(4, n, d))
+    for kv, nt in ((30, 1), (30, 6), (12, 12), (40, 9)):
+        _, dk, dv, _ = O.head_backward(q, k, v, do, causal=True, scale=0.6, kv=kv)
+        tk, tv = impl.head_tail_keys(q, k, v, do, nt, scale=0.6, kv=kv)
+        np.testing.assert_allclose(tk, dk[kv - nt:kv], atol=1e-13)
+        np.testing.assert_allclose(tv, dv[kv - nt:kv], atol=1e-13)
+        assert not dk[kv:].any() and not dv[kv:].any()
+
+
+RPINS = [rpin_rows_match_full, rpin_rows_zero_query, rpin_tail_keys_match_full, rpin_tail_keys_padded_match_full]
 
 
 @pytest.mark.parametrize("pin", RPINS, ids=lambda p: p.__name__)
@@ -439,20 +453,23 @@ def _rows_variant(kind):
 
 
 def _tail_variant(kind):
-    def tail_fn(q, k, v, do, ntail, *, scale):
+    def tail_fn(q, k, v, do, ntail, *, scale, kv=None):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
         n = k.shape[0]
-        j0 = n - ntail
+        hi = n if kv is None else kv
+        j0 = hi - ntail
         dk = np.zeros((ntail, k.shape[1]))
         dv = np.zeros((ntail, v.shape[1]))
         first = j0 + 1 if kind == "skip_first_row" else j0
-        for i in range(first, n):
-            s = scale * (k[: i + 1] @ q[i])
+        last = hi if kind == "rows_stop_at_kv" else n
+        for i in range(first, last):
+            vis = min(i + 1, hi)
+            s = scale * (k[:vis] @ q[i])
             e = np.exp(s - s.max())
             p = e / e.sum()
-            dp = v[: i + 1] @ do[i]
+            dp = v[:vis] @ do[i]
             ds = p * dp - p * (p @ dp)
-            for j in range(j0, i + 1):
+            for j in range(j0, vis):
                 dv[j - j0] += p[j] * do[i]
                 dk[j - j0] += (ds[j] * k[j]) * scale if kind == "dk_uses_k" else scale * ds[j] * q[i]
         return dk, dv
@@ -467,6 +484,8 @@ ROW_MUTANTS = {
     "rows_dq_no_scale": types.SimpleNamespace(head_rows=_rows_variant("dq_no_scale"), head_tail_keys=O.head_tail_keys),
     "tail_skips_first_row": types.SimpleNamespace(head_rows=O.head_rows, head_tail_keys=_tail_variant("skip_first_row")),
     "tail_dk_uses_k": types.SimpleNamespace(head_rows=O.head_rows, head_tail_keys=_tail_variant("dk_uses_k")),
+    "tail_rows_stop_at_kv": types.SimpleNamespace(head_rows=O.head_rows,
+                                                  head_tail_keys=_tail_variant("rows_stop_at_kv")),
 }
 
 

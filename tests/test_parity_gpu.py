@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle.attention as O
 from causal_self_attention_flashattention_amd.inputs import WORKLOADS, make_inputs, make_workload_inputs
 
 from attn_testutil import announce, check_close, compare_all, heads_to_numpy, oracle_ref, require_gpu, run_gpu, to_dev
@@ -91,6 +92,37 @@ def _properties_all_heads(inp_dev, res, kv):
             assert (res["dK"][b, :, n:] == 0).all() and (res["dV"][b, :, n:] == 0).all()
 
 
+def _rows_every_head(inp, res, w, seed, nrand=32, ntail=32):
+    """Every (batch, head): 32 seeded query rows plus tile-boundary rows (O, L, dQ, D) against the
+    row-wise oracle, and the last ntail visible keys' dK, dV against the tail-key oracle, element by
+    element.  A head, rank or per-head base mistake anywhere in the grid shows up here."""
+    B, H, N = w.B, w.H, w.N
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].tolist()
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 129, N - 128, N - 2, N - 1]
+    got = {key: res[key].double().cpu().numpy() for key in ("O", "L", "dQ", "D", "dK", "dV")}
+    for b in range(B):
+        kv = None if kvl is None else kvl[b]
+        hi = N if kv is None else kv
+        for h in range(H):
+            rng = np.random.default_rng(seed * 1000 + b * H + h)
+            extra = [] if kv is None else [kv - 1, min(kv, N - 1)]
+            rows = sorted({r for r in fixed + extra if 0 <= r < N} | set(rng.integers(0, N, nrand).tolist()))
+            q, k, v, do = (inp[n][b, h] for n in ("q", "k", "v", "do"))
+            ro, rl, rdq, rd = O.head_rows(q, k, v, do, rows, causal=w.causal, scale=w.scale, kv=kv)
+            tag = f"(b={b}, h={h})"
+            check_close(f"O rows {tag}", got["O"][b, h][rows], ro, w.dtype)
+            check_close(f"L rows {tag}", got["L"][b, h][rows], rl, w.dtype)
+            check_close(f"dQ rows {tag}", got["dQ"][b, h][rows], rdq, w.dtype)
+            # D's slack for O's bf16 rounding, from the oracle's O (as for the full comparison)
+            slack = 0.0 if w.dtype == "f32" else 2.0 ** -8 * np.abs(ro * do.double().numpy()[rows]).sum(-1)
+            check_close(f"D rows {tag}", got["D"][b, h][rows], rd, w.dtype, slack)
+            if w.causal:
+                nt = min(ntail, hi)
+                tk, tv = O.head_tail_keys(q, k, v, do, nt, scale=w.scale, kv=kv)
+                check_close(f"dK tail keys {tag}", got["dK"][b, h][hi - nt:hi], tk, w.dtype)
+                check_close(f"dV tail keys {tag}", got["dV"][b, h][hi - nt:hi], tv, w.dtype)
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_matches_oracle(name):
     require_gpu()
@@ -104,6 +136,9 @@ def test_workload_matches_oracle(name):
     ref = oracle_ref(inp, w.causal, w.scale, heads)
     rep = compare_all(res, ref, w.dtype, heads)
     announce(f"workload {name} max abs / rel errors: " + ", ".join(f"{k}={v[0]:.3g}/{v[1]:.3g}" for k, v in rep.items()))
+    if FULL_HEADS[name] < w.B * w.H:
+        _rows_every_head(inp, res, w, w.seed)
+        announce(f"workload {name}: sampled rows and tail keys of all {w.B * w.H} heads match")
 
 
 # Scores that climb along the key index (a ramp) or jump at scattered keys (spikes), so the

@@ -1,4 +1,4 @@
-"""GPU parity of the stand-alone D pass (attn_bwd_rowdot): D_i = sum_c O_ic dO_ic ([A2] §4.1, the
+"""GPU parity of the stand-alone D pass (attn_bwd_rowdot): D_i = sum_c O_ic dO_ic ([A2] §4.2.2, the
 D vector of the backward pass with recomputation) against the oracle's rowsum_o_do on the same
 seeded O and dO, for every head dim and both dtypes, with row counts that leave a partial last
 block of rows, and with guard bands around D.  D is defined for any O, so O here is a seeded
