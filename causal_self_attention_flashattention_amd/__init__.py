@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     bwd,
     bwd_workspace_bytes,
     bwd_launches,
+    bwd_noalloc,
     bwd_dkdv,
     bwd_dq,
     fwd,
@@ -20,4 +21,4 @@ from .binding import (  # noqa: F401
 )
 from .function import FlashAttention, flash_attention  # noqa: F401
 
-__all__ = ["FlashAttention", "flash_attention", "fwd", "fwd_workspace_bytes", "bwd", "bwd_workspace_bytes", "bwd_launches", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]
+__all__ = ["FlashAttention", "flash_attention", "fwd", "fwd_workspace_bytes", "bwd", "bwd_workspace_bytes", "bwd_launches", "bwd_noalloc", "rowdot", "bwd_dkdv", "bwd_dq", "supported", "load_library", "status_string", "AttnError"]

@@ -36,6 +36,8 @@ SIGNATURES = {
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "attn_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp,
                          _sz, _vp]),
+    "attn_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                              _vp]),
     "attn_status_string": (ctypes.c_char_p, [_i]),
     "attn_supported": (_i, [_i, _i]),
     "attn_bwd_launches": (_i, [_i, _i, _i, _i, _i]),
@@ -194,6 +196,24 @@ def bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None, kv
                                     _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
                                     _ptr(kv), _ptr(bm), _ptr(workspace), ws_bytes, _stream())
     _check("attn_bwd_ex", st)
+    return dq, dk, dv, D
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def bwd_noalloc(q, k, v, o, do, lse, outs, causal: bool = True, scale: float | None = None, kv_len=None,
+                block_mask=None):
+    """:func:`bwd` through attn_bwd_noalloc: no workspace, the library's static scratch takes the
+    split partials.  ``outs = (dQ, dK, dV, D)`` must be given (nothing is allocated here); kv_len and
+    block_mask, if given, should already be device tensors."""
+    B, H, N, d = _check_qkv(q, k, v, o, do)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq, dk, dv, D = outs
+    st = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                         _ptr(dv), _ptr(D), B, H, N, d, int(bool(causal)), scale, _DTYPES[q.dtype],
+                                         _ptr(kv_len), _ptr(block_mask), _stream())
+    _check("attn_bwd_noalloc", st)
     return dq, dk, dv, D
 
 

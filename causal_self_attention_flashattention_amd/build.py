@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_noalloc.hip", "attn_api.cpp"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

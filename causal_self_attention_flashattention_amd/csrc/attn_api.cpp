@@ -83,6 +83,8 @@ const char* attn_status_string(int status) {
     case ATTN_E_ALIAS: return "an output buffer overlaps an input or another output";
     case ATTN_E_LAUNCH: return "kernel launch failed";
     case ATTN_E_SCALE: return "scale is not a finite number greater than 0";
+    case ATTN_E_SCRATCH:
+      return "the shape needs more scratch than attn_bwd_noalloc's static buffer holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -151,10 +153,13 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   return attn::bwd_workspace_bytes(dtype, p);
 }
 
-int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
-                void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
-                int dtype, const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+}  // extern "C"
+
+namespace attn {
+
+int bwd_ex_check(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                 void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, float scale, int dtype,
+                 const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes) {
   if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !D) return ATTN_E_NULL;
   int st = check_common(B, H, N, d, dtype, scale, true);
   if (st != ATTN_OK) return st;
@@ -171,8 +176,13 @@ int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, cons
   const Range ins[8] = {range_of(Q, tb), range_of(K, tb), range_of(V, tb), range_of(O, tb), range_of(dO, tb),
                         range_of(L, lb), kv_len ? range_of(kv_len, (size_t)B * 4) : Range{0, 0},
                         range_of(block_mask, mb)};
-  st = check_alias(outs, workspace ? 5 : 4, ins, 8);
-  if (st != ATTN_OK) return st;
+  return check_alias(outs, workspace ? 5 : 4, ins, 8);
+}
+
+int bwd_ex_run(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L, void* dQ,
+               void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale, int dtype,
+               const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
   const attn::Problem p{B, H, N, d, causal ? 1 : 0, scale, kv_len, block_mask};
   const size_t need = attn::bwd_workspace_bytes(dtype, p);
   const bool split = need > 0 && workspace && workspace_bytes >= need;
@@ -190,6 +200,21 @@ int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, cons
   if (attn::launch_dq(dtype, p, Q, K, V, dO, O, L, D, dQ, stream, ws, wb) != hipSuccess) return ATTN_E_LAUNCH;
   if (attn::launch_dkdv(dtype, p, Q, K, V, dO, L, D, dK, dV, stream, ws, wb) != hipSuccess) return ATTN_E_LAUNCH;
   return ATTN_OK;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                int dtype, const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  const int st = attn::bwd_ex_check(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, scale, dtype, kv_len, block_mask,
+                                    workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return attn::bwd_ex_run(Q, K, V, O, dO, L, dQ, dK, dV, D, B, H, N, d, causal, scale, dtype, kv_len, block_mask,
+                          workspace, workspace_bytes, stream);
 }
 
 int attn_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,

@@ -55,4 +55,14 @@ hipError_t launch_bwd_small(int dtype, const Problem& p, const void* Q, const vo
                             const void* dO, const void* O, const float* L, float* Dv, void* dQ, void* dK,
                             void* dV, hipStream_t stream);
 
+// attn_bwd_ex split in two: argument validation (returns an attn_status, launches nothing) and
+// dispatch of the kernels (returns ATTN_OK or ATTN_E_LAUNCH); the C ABI runs both.
+int bwd_ex_check(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                 void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, float scale, int dtype,
+                 const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes);
+int bwd_ex_run(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L, void* dQ,
+               void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale, int dtype,
+               const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
 }  // namespace attn

@@ -49,7 +49,8 @@ typedef enum {
   ATTN_E_ALIGN = -5,   /* a pointer is not 16-byte aligned */
   ATTN_E_ALIAS = -6,   /* an output buffer overlaps an input or another output */
   ATTN_E_LAUNCH = -7,  /* a kernel launch failed (HIP error) */
-  ATTN_E_SCALE = -8    /* scale is not a finite number > 0 */
+  ATTN_E_SCALE = -8,   /* scale is not a finite number > 0 */
+  ATTN_E_SCRATCH = -9  /* attn_bwd_noalloc: the shape needs more than ATTN_NOALLOC_SCRATCH_BYTES */
 } attn_status;
 
 /* Forward pass (Algorithm 1 of the handout, §4.2.2, with the causal flag of Problem
@@ -147,6 +148,28 @@ int attn_bwd_ex(const void* Q, const void* K, const void* V, const void* O, cons
                 void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
                 int dtype, const int32_t* kv_len, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
+
+/* Size of the static device scratch behind attn_bwd_noalloc (64 MiB per GPU the library runs on). */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* attn_bwd_ex without a caller workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Where attn_bwd_ex would
+ * split the workgroup chains of a small grid (attn_bwd_workspace_bytes(...) > 0), the partial sums go
+ * to a file-scope device array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the call itself calls no hipMalloc, hipFree or allocating library
+ * routine.  Results are bitwise those of attn_bwd_ex given a workspace of at least
+ * attn_bwd_workspace_bytes(...) bytes.
+ *   Arguments as for attn_bwd_ex (no workspace).  The scratch is that of the device `stream` belongs
+ *   to (the current device for the NULL stream).
+ *   ATTN_E_SCRATCH when attn_bwd_workspace_bytes(B, H, N, d, dtype) > ATTN_NOALLOC_SCRATCH_BYTES
+ *   (nothing is enqueued); other errors as for attn_bwd_ex.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents (each call
+ * writes every partial it later reads, so nothing needs clearing): calls whose kernels can overlap
+ * on one GPU (different streams, or different host threads without ordering) race and must not be
+ * issued. */
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                     void* dQ, void* dK, void* dV, float* D, int B, int H, int N, int d, int causal, float scale,
+                     int dtype, const int32_t* kv_len, const uint8_t* block_mask, hipStream_t stream);
 
 /* How many kernels attn_bwd launches for this problem: 1 when the dQ and dK/dV work share one
  * launch (small bfloat16 problems with d <= 80, where the grid would otherwise leave CUs idle),

@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 ATTN_OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH, E_SCALE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+E_SCRATCH = -9
 
 
 def declared_functions():
@@ -45,7 +46,7 @@ def test_exported_symbols_have_c_linkage():
 
 def test_version_and_status_strings(lib):
     assert lib.attn_version() == 10000
-    for st in (ATTN_OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH, E_SCALE):
+    for st in (ATTN_OK, E_NULL, E_SHAPE, E_HEADDIM, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH, E_SCALE, E_SCRATCH):
         s = bnd.status_string(st)
         assert s and s != "unknown status"
     assert bnd.status_string(12345) == "unknown status"
@@ -208,3 +209,26 @@ def test_workspace_queries(lib):
     # the workspace scales with the planned chunks, never beyond 16 partial copies of the output
     w = lib.attn_fwd_workspace_bytes(1, 1, 16384, 128, 1)
     assert 0 < w <= 16 * 16384 * (128 + 2) * 4
+
+
+def _bwd_noalloc(lib, **kw):
+    p = dict(Q=A, K=A + SZ, V=A + 2 * SZ, O=A + 3 * SZ, dO=A + 4 * SZ, L=A + 5 * SZ, dQ=A + 6 * SZ,
+             dK=A + 7 * SZ, dV=A + 8 * SZ, D=A + 9 * SZ, B=1, H=1, N=16384, d=128, causal=1, scale=0.125, dtype=1,
+             kv=None, mask=None)
+    p.update(kw)
+    return lib.attn_bwd_noalloc(p["Q"], p["K"], p["V"], p["O"], p["dO"], p["L"], p["dQ"], p["dK"], p["dV"], p["D"],
+                                p["B"], p["H"], p["N"], p["d"], p["causal"], p["scale"], p["dtype"], p["kv"],
+                                p["mask"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), E_SCRATCH),                           # needs 160 MiB of split partials > 64 MiB
+    (dict(B=1, H=1, N=65536, d=128), E_SCRATCH),
+    (dict(dQ=None), E_NULL), (dict(d=48), E_HEADDIM), (dict(scale=0.0), E_SCALE),
+    (dict(dK=A), E_ALIAS), (dict(Q=A + 2), E_ALIGN),
+    (dict(N=(1 << 23) + 64), E_SHAPE),
+])
+def test_bwd_noalloc_rejects_bad_arguments(lib, kw, status):
+    # argument errors take precedence; a valid shape whose split partials exceed the static scratch
+    # is refused before anything touches the GPU
+    assert _bwd_noalloc(lib, **kw) == status
