@@ -21,6 +21,11 @@
 
 namespace attn {
 
+#ifndef ATTN_BWD_STORE_EARLY
+#define ATTN_BWD_STORE_EARLY 1
+#endif
+constexpr bool kBwdStoreEarly = ATTN_BWD_STORE_EARLY;
+
 // ------------------------------------------------------------------------------------------
 // D = rowsum(O o dO)
 
@@ -323,6 +328,13 @@ __device__ __forceinline__ void dkdv_body(
     if (nxt < qt_hi) load_stage(nxt);
 
     for (int it = 0; cur < qt_hi; ++it) {
+      int nxt2 = qt_hi;
+      if constexpr (kBwdStoreEarly && D > 80) {
+        // the next stage (loaded one iteration ago) goes to LDS before this stage's products
+        nxt2 = nxt < qt_hi ? after(nxt) : qt_hi;
+        if (nxt < qt_hi) store_stage(lds + ((it + 1) & 1) * STAGE);
+        if (nxt2 < qt_hi) load_stage(nxt2);
+      }
       const int q0 = cur * BQS;
       const lds_t* qtile = lds + (it & 1) * STAGE;
       const lds_t* otile = qtile + TILE;
@@ -414,10 +426,14 @@ __device__ __forceinline__ void dkdv_body(
           }
         }
       }
-      const int nxt2 = nxt < qt_hi ? after(nxt) : qt_hi;
-      if (nxt < qt_hi) store_stage(lds + ((it + 1) & 1) * STAGE);
-      __syncthreads();
-      if (nxt2 < qt_hi) load_stage(nxt2);
+      if constexpr (kBwdStoreEarly && D > 80) {
+        __syncthreads();
+      } else {
+        nxt2 = nxt < qt_hi ? after(nxt) : qt_hi;
+        if (nxt < qt_hi) store_stage(lds + ((it + 1) & 1) * STAGE);
+        __syncthreads();
+        if (nxt2 < qt_hi) load_stage(nxt2);
+      }
       cur = nxt;
       nxt = nxt2;
     }
@@ -713,6 +729,20 @@ __device__ __forceinline__ void dq_body(
     vc.load(rv, nxt * BKT);
   }
   for (int it = 0; cur < t_hi; ++it) {
+    int nxt2 = t_hi;
+    if constexpr (kBwdStoreEarly && D > 80) {
+      // the next tile (loaded one iteration ago) goes to LDS before this tile's products
+      nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+      if (nxt < t_hi) {
+        lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
+        kc.store(st);
+        vc.store(st + TILE);
+      }
+      if (nxt2 < t_hi) {
+        kc.load(rk, nxt2 * BKT);
+        vc.load(rv, nxt2 * BKT);
+      }
+    }
     // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
     const lds_t* ktile = lds + (it & 1) * 2 * TILE + grp * BK * LD * (int)sizeof(T);
     const lds_t* vtile = ktile + TILE;
@@ -752,16 +782,20 @@ __device__ __forceinline__ void dq_body(
         }
       }
     }
-    const int nxt2 = nxt < t_hi ? after(nxt) : t_hi;
-    if (nxt < t_hi) {
-      lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
-      kc.store(st);
-      vc.store(st + TILE);
-    }
-    __syncthreads();
-    if (nxt2 < t_hi) {
-      kc.load(rk, nxt2 * BKT);
-      vc.load(rv, nxt2 * BKT);
+    if constexpr (kBwdStoreEarly && D > 80) {
+      __syncthreads();
+    } else {
+      nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+      if (nxt < t_hi) {
+        lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
+        kc.store(st);
+        vc.store(st + TILE);
+      }
+      __syncthreads();
+      if (nxt2 < t_hi) {
+        kc.load(rk, nxt2 * BKT);
+        vc.load(rv, nxt2 * BKT);
+      }
     }
     cur = nxt;
     nxt = nxt2;

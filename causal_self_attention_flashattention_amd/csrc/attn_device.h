@@ -138,6 +138,22 @@ constexpr int lds_pitch() {
   return bytes / (int)sizeof(T);
 }
 
+// LDS row pitch (in elements) of a tile that is only read with transposing reads (frag_trans).
+// Measured on gfx950 for bfloat16 tiles, the transposing reads run at ~210 B/clk per CU when the
+// pitch is 64 bytes modulo 128 and at ~155 B/clk at every other 16-byte-aligned pitch tried (while
+// 16-byte reads of 32 consecutive rows then drop to ~80 B/clk, so tiles read both ways keep
+// lds_pitch).  float32 tiles are read with plain 4-byte reads and keep lds_pitch.
+template <typename T, int DP>
+constexpr int lds_pitch_tr() {
+  if constexpr (sizeof(T) != 2) {
+    return lds_pitch<T, DP>();
+  } else {
+    int bytes = DP * (int)sizeof(T);
+    while (bytes % 128 != 64) bytes += 16;
+    return bytes / (int)sizeof(T);
+  }
+}
+
 // Exchange a value with the lane 32 positions away (lanes l and l ^ 32 hold the two halves of
 // an accumulator column).
 __device__ __forceinline__ float swap_halves(float x) {

@@ -27,6 +27,10 @@ constexpr float kSumBound = 256.0f;  // 2^kRescaleSlack
 // Head dims up to 64, where the softmax's vector work per key outweighs the matrix products, form
 // the weights before taking the row max (see the tile loop); larger ones take the max first.
 constexpr int kSumCheckMaxD = 64;
+#ifndef ATTN_STORE_EARLY
+#define ATTN_STORE_EARLY 1
+#endif
+constexpr bool kStoreEarly = ATTN_STORE_EARLY;
 
 // With SPLIT the key range of every query tile is cut into `nsplit` chunks, one workgroup each;
 // a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
@@ -54,8 +58,13 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;             // key blocks per wave and tile
   constexpr int BKT = G * BK;             // keys per tile
-  constexpr int LD = lds_pitch<T, DP>();  // LDS row stride (elements)
-  constexpr int TILE = BKT * LD * (int)sizeof(T);  // bytes of one K or V tile
+  constexpr int LD = lds_pitch<T, DP>();     // LDS row stride of K tiles (elements)
+  // ... of V tiles, which are only read transposed (up to d = 64 the larger pitch would cost a
+  // workgroup per CU: four of them fill the LDS with the K pitch)
+  constexpr int LDV = DP > 64 ? lds_pitch_tr<T, DP>() : LD;
+  constexpr int TILE = BKT * LD * (int)sizeof(T);    // bytes of one K tile
+  constexpr int TILEV = BKT * LDV * (int)sizeof(T);  // bytes of one V tile
+  constexpr int STG = TILE + TILEV;                  // bytes of one stage (K tile, then V tile)
   constexpr int SHIFT = BK == 64 ? 0 : 1;          // key tiles per mask block = 1 << SHIFT
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
@@ -64,9 +73,9 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 
   // Two stages of (K tile, V tile): the next tile is written while the current one is read; then,
   // for block-sparse calls, one byte per mask column (which of this workgroup's rows see it).
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + (BSP ? kMaxMaskBlocks : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STG + (BSP ? kMaxMaskBlocks : 0)];
   lds_t* lds = (lds_t*)smem;
-  lds_t* map = lds + 4 * TILE;
+  lds_t* map = lds + 2 * STG;
 
   const int TQ = (N + QT - 1) / QT;
   const int nsp = SPLIT ? nsplit : 1;
@@ -128,8 +137,8 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   bool first = true;  // no tile run yet: the running max starts from the first tile's max
 
   if constexpr (DP > D) {
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + TILE);
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 3 * TILE);
+    zero_pad_cols<T, BKT, D, LDV, DP, NT>(lds + TILE);
+    zero_pad_cols<T, BKT, D, LDV, DP, NT>(lds + STG + TILE);
   }
   // Key tiles in loop order: all of [0, nkt), or (block-sparse) those some row of this workgroup
   // may see; the current, next and next-but-one tiles are tracked for the two-stage pipeline.
@@ -140,7 +149,8 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     cur = next_live_tile(map, t_lo, t_hi, SHIFT);
   }
   auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
-  TileCopy<T, BKT, D, LD, NT> kc, vc;
+  TileCopy<T, BKT, D, LD, NT> kc;
+  TileCopy<T, BKT, D, LDV, NT> vc;
   if (cur < t_hi) {
     kc.load(rk, cur * BKT);
     vc.load(rv, cur * BKT);
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   // The Q fragments (or rows) were requested first: waiting for them here leaves the first K/V
   // tile's loads in flight, so the two memory latencies overlap.
   if constexpr (STQ) {
-    qst.store(lds + 2 * TILE);
+    qst.store(lds + STG);
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   __syncthreads();
   if constexpr (STQ) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = M::frag_direct(lds + 2 * TILE, LD, 32 * w * LD + ks * M::KSTEP);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = M::frag_direct(lds + STG, LD, 32 * w * LD + ks * M::KSTEP);
     __syncthreads();  // every wave holds its fragments before the first iteration refills the slot
   }
   int nxt = cur < t_hi ? after(cur) : t_hi;
@@ -168,11 +178,30 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     kc.load(rk, nxt * BKT);
     vc.load(rv, nxt * BKT);
   }
+  // Where the next tile is written to LDS: at the start of each iteration (d = 128, where it was
+  // measured faster: the writes overlap the tile's products) or right before the barrier.
+  constexpr bool EARLY = kStoreEarly && D > 80;
 
   for (int it = 0; cur < t_hi; ++it) {
+    int nxt2 = t_hi;
+    if constexpr (EARLY) {
+      // The next tile (loaded one iteration ago) goes to LDS at the start of the iteration, into
+      // the stage every wave finished reading before the last barrier, so the LDS writes overlap
+      // this tile's products instead of stalling every wave right before the barrier.
+      nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+      if (nxt < t_hi) {
+        lds_t* st = lds + ((it + 1) & 1) * STG;
+        kc.store(st);
+        vc.store(st + TILE);
+      }
+      if (nxt2 < t_hi) {
+        kc.load(rk, nxt2 * BKT);
+        vc.load(rv, nxt2 * BKT);
+      }
+    }
     // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
-    const lds_t* ktile = lds + (it & 1) * 2 * TILE + grp * BK * LD * (int)sizeof(T);
-    const lds_t* vtile = ktile + TILE;
+    const lds_t* ktile = lds + (it & 1) * STG + grp * BK * LD * (int)sizeof(T);
+    const lds_t* vtile = lds + (it & 1) * STG + TILE + grp * BK * LDV * (int)sizeof(T);
     const int k0 = cur * BKT + grp * BK;
     // (k0 is a multiple of 64 and qw of 32, so a wave that runs has key k0 visible in every row.)
     bool run = wave_live && k0 < kend && !(causal && k0 > qw_last);
@@ -269,19 +298,23 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
         for (int c = 0; c < M::CALLS32; ++c)
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            o[db] = M::mma(M::frag_trans(vtile, LD, nb * 32 * LD + db * 32, c), pf[c], o[db]);
+            o[db] = M::mma(M::frag_trans(vtile, LDV, nb * 32 * LDV + db * 32, c), pf[c], o[db]);
       }
     }
-    const int nxt2 = nxt < t_hi ? after(nxt) : t_hi;
-    if (nxt < t_hi) {
-      lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
-      kc.store(st);
-      vc.store(st + TILE);
-    }
-    __syncthreads();
-    if (nxt2 < t_hi) {
-      kc.load(rk, nxt2 * BKT);
-      vc.load(rv, nxt2 * BKT);
+    if constexpr (EARLY) {
+      __syncthreads();
+    } else {
+      nxt2 = nxt < t_hi ? after(nxt) : t_hi;
+      if (nxt < t_hi) {
+        lds_t* st = lds + ((it + 1) & 1) * STG;
+        kc.store(st);
+        vc.store(st + TILE);
+      }
+      __syncthreads();
+      if (nxt2 < t_hi) {
+        kc.load(rk, nxt2 * BKT);
+        vc.load(rv, nxt2 * BKT);
+      }
     }
     cur = nxt;
     nxt = nxt2;
@@ -291,7 +324,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     // Group 1 hands (m, l, O) to the wave of group 0 that owns the same queries; the tiles are no
     // longer read (the loop ended on a barrier and staged nothing after it).
     constexpr int F = 2 + 16 * NDB;  // floats per lane
-    static_assert(NW * 64 * F * 4 <= 4 * TILE, "merge buffer fits in the tile stages");
+    static_assert(NW * 64 * F * 4 <= 2 * STG, "merge buffer fits in the tile stages");
     float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
     if (grp == 1) {
       mrg[0] = m_run;
