@@ -25,6 +25,10 @@ namespace attn {
 #define ATTN_BWD_STORE_EARLY 1
 #endif
 constexpr bool kBwdStoreEarly = ATTN_BWD_STORE_EARLY;
+#ifndef ATTN_XCD_MAP
+#define ATTN_XCD_MAP 1
+#endif
+constexpr bool kXcdMap = ATTN_XCD_MAP;
 
 // ------------------------------------------------------------------------------------------
 // D = rowsum(O o dO)
@@ -106,7 +110,7 @@ constexpr int dkdv_lds_bytes() {
 // are cut into `nsplit` chunks, one workgroup each, which write unscaled float32 partial dK and dV
 // rows to `part` ([nsplit][BH*N][D] for dK, then the same for dV) for bwd_sum_kernel to add up.
 template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, bool SPLIT = false,
-          int G = 1>
+          int G = 1, bool XCD = false>
 __device__ __forceinline__ void dkdv_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse,
@@ -139,7 +143,7 @@ __device__ __forceinline__ void dkdv_body(
 
   const int TK = (N + KT - 1) / KT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = rank_major_block(BH, TK * nsp, block);
+  const int logical = XCD ? xcd_block(BH, TK * nsp, block) : rank_major_block(BH, TK * nsp, block);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TK;
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void dkdv_kernel(
     int BH, int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
     const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem[dkdv_lds_bytes<T, D, NW, BQ, false, VLDS, KB, BSP, G>()];
-  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP, SPLIT, G>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV,
+  dkdv_body<T, D, NW, BQ, false, VLDS, KB, BSP, SPLIT, G, kXcdMap>(smem, blockIdx.x, Q, K, V, dO, nullptr, Lse, Dv, dK, dV,
                                                           BH, H, N, causal, scale, scale_log2, kv_len, bmask, nsplit,
                                                           part);
 }
@@ -575,7 +579,8 @@ template <typename T, int D, int NW>
 constexpr int dq_stq_bytes() {
   return 3 * 32 * NW * lds_pitch<T, (D + 31) / 32 * 32>() * (int)sizeof(T);
 }
-template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false, int G = 1, bool STQ = false>
+template <typename T, int D, int NW, int BK, bool BSP = false, bool SPLIT = false, int G = 1, bool STQ = false,
+          bool XCD = false>
 __device__ __forceinline__ void dq_body(
     char* smem, int block, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ Oin, const float* __restrict__ Lse, float* __restrict__ Dv,
@@ -606,7 +611,7 @@ __device__ __forceinline__ void dq_body(
 
   const int TQ = (N + QT - 1) / QT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = rank_major_block(BH, TQ * nsp, block);
+  const int logical = XCD ? xcd_block(BH, TQ * nsp, block) : rank_major_block(BH, TQ * nsp, block);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TQ;
@@ -879,7 +884,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void dq_kernel(
     int H, int N, int causal, float scale, float scale_log2, const int32_t* __restrict__ kv_len,
     const uint8_t* __restrict__ bmask, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<T, D, G * BK, BSP>()];
-  dq_body<T, D, NW, BK, BSP, SPLIT, G>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale,
+  dq_body<T, D, NW, BK, BSP, SPLIT, G, false, kXcdMap>(smem, blockIdx.x, Q, K, V, dO, Oin, Lse, Dv, dQ, BH, H, N, causal, scale,
                                        scale_log2, kv_len, bmask, nsplit, part);
 }
 

@@ -267,6 +267,43 @@ __device__ __forceinline__ int rank_major_block(int nheads, int nranks, int b) {
   return (b % nheads) * nranks + b / nheads;
 }
 
+// Block index -> logical work item (as rank_major_block) with each head's items kept on one XCD
+// where that can be balanced.  The 8 XCDs receive blocks round-robin (block b runs on XCD b % 8,
+// in order b / 8 there), and each XCD has its own L2: the items of a head that share its K and V
+// rows should run on one XCD.  With nheads = 8 hq + hr (0 < hr), XCD x takes whole heads
+// x hq .. x hq + hq - 1 and a share of the hr remaining heads by rank: when hr divides 8, remaining
+// head j goes to the 8 / hr XCDs j (8 / hr) + (r mod 8 / hr) (so each is split over that many),
+// otherwise rank r of remaining head j goes to XCD (r + j) mod 8.  Every XCD then holds the same
+// number of items of the same mix of ranks (balanced causal work), and runs them rank-major,
+// heaviest first.  Needs nranks to be a multiple of the period of that split; otherwise, and when
+// nheads is a multiple of 8 (where rank-major order already keeps each head on one XCD), it is
+// rank_major_block.  A bijection from [0, nheads nranks) onto the items.
+__device__ __forceinline__ int xcd_block(int nheads, int nranks, int b) {
+  constexpr int NX = 8;
+  const int hq = nheads / NX, hr = nheads % NX;
+  const bool divides = hr > 0 && NX % hr == 0;
+  const int T = divides ? NX / hr : NX;  // ranks per period of the split
+  if (hr == 0 || nranks % T != 0 || b >= nheads * nranks) return rank_major_block(nheads, nranks, b);
+  const int x = b % NX, i = b / NX;
+  const int P = T * hq + (divides ? 1 : hr);  // items of XCD x per period
+  const int p = i / P;
+  int q = i % P;
+  for (int rp = 0; rp < T; ++rp) {
+    const int r = p * T + rp;
+    int j;  // remaining head that XCD x serves at rank r, or -1
+    if (divides) {
+      j = (r % T == x % T) ? x / T : -1;
+    } else {
+      j = ((x - r) % NX + NX) % NX;
+      if (j >= hr) j = -1;
+    }
+    const int n = hq + (j >= 0 ? 1 : 0);
+    if (q < n) return (q < hq ? x * hq + q : NX * hq + j) * nranks + r;
+    q -= n;
+  }
+  return -1;  // not reached: the P items of a period are enumerated above
+}
+
 // ------------------------------------------------------------------------------------------
 // Block-sparse masks.  A mask is uint8 [TB][TB], TB = ceil(N / kMaskBlock), row-major, shared by
 // every (batch, head): entry (r, c) non-zero lets queries [64r, 64r + 64) attend keys

@@ -31,6 +31,10 @@ constexpr int kSumCheckMaxD = 64;
 #define ATTN_STORE_EARLY 1
 #endif
 constexpr bool kStoreEarly = ATTN_STORE_EARLY;
+#ifndef ATTN_XCD_MAP
+#define ATTN_XCD_MAP 1
+#endif
+constexpr bool kXcdMap = ATTN_XCD_MAP;
 
 // With SPLIT the key range of every query tile is cut into `nsplit` chunks, one workgroup each;
 // a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 
   const int TQ = (N + QT - 1) / QT;
   const int nsp = SPLIT ? nsplit : 1;
-  const int logical = rank_major_block(BH, TQ * nsp, blockIdx.x);
+  const int logical = kXcdMap ? xcd_block(BH, TQ * nsp, blockIdx.x) : rank_major_block(BH, TQ * nsp, blockIdx.x);
   if (logical < 0) return;
   const int split = logical % nsp;
   const int bh = logical / nsp / TQ;

@@ -47,6 +47,15 @@ SMALL += [
     ("bf16", 1, 2, 600, 32, True, [550]),
     ("bf16", 2, 1, 513, 16, False, None),
     ("bf16", 1, 3, 1100, 64, False, [1000]),
+    # head counts that are not multiples of 8 with tile counts that are multiples of the split
+    # period, so the XCD-aware block order (heads shared between XCDs by rank) is the one used
+    ("bf16", 1, 36, 1024, 128, True, None),
+    ("bf16", 1, 12, 1024, 64, True, [1000]),
+    ("bf16", 1, 5, 1024, 64, False, None),
+    ("bf16", 1, 7, 2048, 64, True, None),
+    ("bf16", 3, 3, 1024, 128, True, [1024, 900, 700]),
+    ("bf16", 1, 6, 1024, 80, True, None),
+    ("bf16", 2, 1, 1024, 64, True, None),
 ]
 
 
