@@ -91,7 +91,7 @@ constexpr int kDselfMaxN = 4096;
 template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, int G = 1>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
-  constexpr int TILE = G * BQ * lds_pitch<T, DP>() * (int)sizeof(T);
+  constexpr int TILE = StageTile<T, D>::bytes(G * BQ);
   return 2 * (2 * TILE + 2 * G * BQ * (int)sizeof(float)) + (DSELF ? kDselfMaxN * (int)sizeof(float) : 0) +
          (VLDS ? 32 * KB * NW * lds_pitch<T, DP>() * (int)sizeof(T) : 0) + (BSP ? kMaxMaskBlocks : 0);
 }
@@ -126,8 +126,9 @@ __device__ __forceinline__ void dkdv_body(
   constexpr int KS = D / M::KSTEP;
   constexpr int NQB = BQ / 32;   // query blocks per wave and stage
   constexpr int BQS = G * BQ;    // query rows per stage
-  constexpr int LD = lds_pitch<T, DP>();
-  constexpr int TILE = BQS * LD * (int)sizeof(T);
+  constexpr int LD = lds_pitch<T, DP>();  // V rows (VLDS)
+  using ST = StageTile<T, D>;              // Q and dO tiles (read directly and transposed)
+  constexpr int TILE = ST::bytes(BQS);
   constexpr int STAGE = 2 * TILE + 2 * BQS * (int)sizeof(float);  // Q tile, dO tile, L row, D row
   constexpr int SHIFT = BQ == 64 ? 0 : 1;                         // query tiles per mask block = 1 << SHIFT
   static_assert(2 * BQS <= NT, "one thread per staged L / D value");
@@ -198,15 +199,16 @@ __device__ __forceinline__ void dkdv_body(
           if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
         }
     }
+    const StageReader<T, D> sr;
     auto settle_kv = [&]() {
       if constexpr (STK) {
-        kst.store(lds + STAGE);
-        vst.store(lds + STAGE + TILE);
+        kst.template store_to<ST>(lds + STAGE);
+        vst.template store_to<ST>(lds + STAGE + TILE);
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kf[0][ks] = M::frag_direct(lds + STAGE, LD, KW * w * LD + ks * M::KSTEP);
-          vf[0][ks] = M::frag_direct(lds + STAGE + TILE, LD, KW * w * LD + ks * M::KSTEP);
+          kf[0][ks] = sr.direct(lds + STAGE, KW * w, ks);
+          vf[0][ks] = sr.direct(lds + STAGE + TILE, KW * w, ks);
         }
       } else {
 #pragma unroll
@@ -231,10 +233,10 @@ __device__ __forceinline__ void dkdv_body(
     // DSELF: D for rows [qt0*BQS, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
     if constexpr (DP > D) {
-      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds);
-      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + TILE);
-      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + STAGE);
-      zero_pad_cols<T, BQS, D, LD, DP, NT>(lds + STAGE + TILE);
+      zero_pad_stage<ST, T, BQS, D, NT>(lds);
+      zero_pad_stage<ST, T, BQS, D, NT>(lds + TILE);
+      zero_pad_stage<ST, T, BQS, D, NT>(lds + STAGE);
+      zero_pad_stage<ST, T, BQS, D, NT>(lds + STAGE + TILE);
     }
     TileCopy<T, BQS, D, LD, NT> qc, oc;
     // One staged value per thread: L (threads < BQS) or D (threads BQS..2BQS-1).  L is scaled to
@@ -250,8 +252,8 @@ __device__ __forceinline__ void dkdv_body(
                                  __builtin_amdgcn_raw_buffer_load_b32(t < BQS ? rl : rd, (qt * BQS + (t % BQS)) * 4, 0, 0));
     };
     auto store_stage = [&](lds_t* st) {
-      qc.store(st);
-      oc.store(st + TILE);
+      qc.template store_to<ST>(st);
+      oc.template store_to<ST>(st + TILE);
       if (threadIdx.x < (DSELF ? BQS : 2 * BQS))
         reinterpret_cast<__attribute__((address_space(3))) float*>(st + 2 * TILE)[threadIdx.x] =
             threadIdx.x < BQS ? lrd * kLog2e : -lrd;
@@ -367,8 +369,8 @@ __device__ __forceinline__ void dkdv_body(
           for (int kb = 0; kb < KB; ++kb) { s[kb] = f32x16{}; dp[kb] = nd; }
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const typename M::frag qa = M::frag_direct(qtile, LD, qb * 32 * LD + ks * M::KSTEP);
-            const typename M::frag oa = M::frag_direct(otile, LD, qb * 32 * LD + ks * M::KSTEP);
+            const typename M::frag qa = sr.direct(qtile, qb * 32, ks);
+            const typename M::frag oa = sr.direct(otile, qb * 32, ks);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               s[kb] = M::mma(qa, kf[kb][ks], s[kb]);
@@ -419,8 +421,8 @@ __device__ __forceinline__ void dkdv_body(
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              const typename M::frag ot = M::frag_trans(otile, LD, qb * 32 * LD + db * 32, c);
-              const typename M::frag qt = M::frag_trans(qtile, LD, qb * 32 * LD + db * 32, c);
+              const typename M::frag ot = sr.trans(otile, qb * 32, db, c);
+              const typename M::frag qt = sr.trans(qtile, qb * 32, db, c);
 #pragma unroll
               for (int kb = 0; kb < KB; ++kb) {
                 dv[kb][db] = M::mma(ot, pf[kb], dv[kb][db]);
@@ -563,8 +565,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void dkdv_kernel(
 
 template <typename T, int D, int BK, bool BSP = false>
 constexpr int dq_lds_bytes() {
-  constexpr int DP = (D + 31) / 32 * 32;
-  return 4 * BK * lds_pitch<T, DP>() * (int)sizeof(T) + (BSP ? kMaxMaskBlocks : 0);
+  return 4 * StageTile<T, D>::bytes(BK) + (BSP ? kMaxMaskBlocks : 0);
 }
 
 // With G = 2 the workgroup has two groups of NW waves over the same queries and key tiles of 2 BK
@@ -598,8 +599,9 @@ __device__ __forceinline__ void dq_body(
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;      // key blocks per wave and tile
   constexpr int BKT = G * BK;      // keys per tile
-  constexpr int LD = lds_pitch<T, DP>();
-  constexpr int TILE = BKT * LD * (int)sizeof(T);
+  constexpr int LD = lds_pitch<T, DP>();  // staged query rows (STQ)
+  using ST = StageTile<T, D>;              // K and V tiles
+  constexpr int TILE = ST::bytes(BKT);
   constexpr int SHIFT = BK == 64 ? 0 : 1;  // key tiles per mask block = 1 << SHIFT
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
                 "block-sparse tiles must nest in the 64 x 64 mask blocks");
@@ -672,8 +674,8 @@ __device__ __forceinline__ void dq_body(
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   if constexpr (DP > D) {
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds);
-    zero_pad_cols<T, BKT, D, LD, DP, NT>(lds + 2 * TILE);
+    zero_pad_stage<ST, T, BKT, D, NT>(lds);
+    zero_pad_stage<ST, T, BKT, D, NT>(lds + 2 * TILE);
   }
   // Key tiles in loop order (all, or the block-sparse live ones), as in the forward.
   int cur = t_lo;
@@ -724,11 +726,12 @@ __device__ __forceinline__ void dq_body(
   settle(lq);
   settle(dq_);
   if (cur < t_hi) {
-    kc.store(lds);
-    vc.store(lds + TILE);
+    kc.template store_to<ST>(lds);
+    vc.template store_to<ST>(lds + TILE);
   }
   __syncthreads();
   int nxt = cur < t_hi ? after(cur) : t_hi;
+  const StageReader<T, D> sr;
   if (nxt < t_hi) {
     kc.load(rk, nxt * BKT);
     vc.load(rv, nxt * BKT);
@@ -740,8 +743,8 @@ __device__ __forceinline__ void dq_body(
       nxt2 = nxt < t_hi ? after(nxt) : t_hi;
       if (nxt < t_hi) {
         lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
-        kc.store(st);
-        vc.store(st + TILE);
+        kc.template store_to<ST>(st);
+        vc.template store_to<ST>(st + TILE);
       }
       if (nxt2 < t_hi) {
         kc.load(rk, nxt2 * BKT);
@@ -749,7 +752,7 @@ __device__ __forceinline__ void dq_body(
       }
     }
     // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
-    const lds_t* ktile = lds + (it & 1) * 2 * TILE + grp * BK * LD * (int)sizeof(T);
+    const lds_t* ktile = lds + (it & 1) * 2 * TILE + ST::block(grp * BK);
     const lds_t* vtile = ktile + TILE;
     bool run = wave_live;
     if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
@@ -766,8 +769,8 @@ __device__ __forceinline__ void dq_body(
         for (int e = 0; e < 16; ++e) dp[e] = D > 80 ? -dq_ : 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = M::mma(M::frag_direct(ktile, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s);
-          dp = M::mma(M::frag_direct(vtile, LD, nb * 32 * LD + ks * M::KSTEP), of[ks], dp);
+          s = M::mma(sr.direct(ktile, nb * 32, ks), qf[ks], s);
+          dp = M::mma(sr.direct(vtile, nb * 32, ks), of[ks], dp);
         }
         if ((causal && kb0 + 31 > qw) || (kb0 + 32 > kv)) {
 #pragma unroll
@@ -783,7 +786,7 @@ __device__ __forceinline__ void dq_body(
           const typename M::frag sf = M::acc_frag(dp, c);
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            acc[db] = M::mma(M::frag_trans(ktile, LD, nb * 32 * LD + db * 32, c), sf, acc[db]);
+            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf, acc[db]);
         }
       }
     }
@@ -793,8 +796,8 @@ __device__ __forceinline__ void dq_body(
       nxt2 = nxt < t_hi ? after(nxt) : t_hi;
       if (nxt < t_hi) {
         lds_t* st = lds + ((it + 1) & 1) * 2 * TILE;
-        kc.store(st);
-        vc.store(st + TILE);
+        kc.template store_to<ST>(st);
+        vc.template store_to<ST>(st + TILE);
       }
       __syncthreads();
       if (nxt2 < t_hi) {

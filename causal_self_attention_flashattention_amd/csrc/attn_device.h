@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_layout.h"
+
 namespace attn {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -53,19 +55,23 @@ template <> struct Mfma<__bf16> {
   // (row0, col0).  One 16-byte LDS read per lane.
   __device__ __forceinline__ static frag frag_direct(const lds_t* tile, int ld, int off) {
     const int l = lane_id();
-    const int e = off + (l & 31) * ld + KPL * (l >> 5);
-    return *reinterpret_cast<const __attribute__((address_space(3))) frag*>(tile + 2 * e);
+    const int e = off + lds::direct_row(l) * ld + lds::direct_byte(l, 0) / 2;
+    return frag_at(tile + 2 * e);
   }
   // 32-column operand whose reduction runs down tile rows in accumulator row order, for the
   // c-th instruction of a 32-row block: slot s of lane l takes tile row
   // 16c + 8(s/4) + 4(l/32) + s%4 and column l % 32 (relative to `off`).
   __device__ __forceinline__ static frag frag_trans(const lds_t* tile, int ld, int off, int c) {
     const int l = lane_id();
-    const int g = l >> 4, j = l & 15;
-    const int row = 16 * c + 4 * (g >> 1) + (j >> 2);
-    const int col = 16 * (g & 1) + 4 * (j & 3);
-    const lds_t* p0 = tile + 2 * (off + row * ld + col);
-    const lds_t* p1 = p0 + 2 * 8 * ld;
+    const lds_t* p0 = tile + 2 * (off + lds::trans_row(l, c, 0) * ld + lds::trans_byte(l, 0) / 2);
+    return frag_tr_at(p0, p0 + 2 * 8 * ld);
+  }
+  // The 16 bytes at p as an operand fragment.
+  __device__ __forceinline__ static frag frag_at(const lds_t* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) frag*>(p);
+  }
+  // The transposing reads at p0 (slots 0-3) and p1 (slots 4-7) as an operand fragment.
+  __device__ __forceinline__ static frag frag_tr_at(const lds_t* p0, const lds_t* p1) {
     i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
     i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
     frag f;
@@ -125,34 +131,91 @@ template <> struct Mfma<float> {
   }
 };
 
-// LDS row pitch (in elements) of a tile whose rows hold DP elements of T.  Two read patterns touch
-// these tiles: 16-byte-per-lane reads of 32 consecutive rows (operands whose reduction runs along a
-// row) and 8-byte transposing reads of 4-row x 16-column blocks.  Measured on gfx950, the first
-// runs at full rate only when the pitch is 16 bytes modulo 32, and the second drops to half rate
-// when the pitch is within 16 bytes of a multiple of 256; the pitch below satisfies both.
+// LDS row pitch (in elements) of a padded tile whose rows hold DP elements of T and are read both
+// as 32-row operands and transposed (lds::padded_pitch).
 template <typename T, int DP>
 constexpr int lds_pitch() {
-  int bytes = DP * (int)sizeof(T) + 16;
-  const int m = bytes % 256;
-  if (m == 0 || m == 16 || m == 240) bytes += 32;
-  return bytes / (int)sizeof(T);
+  return lds::padded_pitch(DP * (int)sizeof(T)) / (int)sizeof(T);
 }
 
-// LDS row pitch (in elements) of a tile that is only read with transposing reads (frag_trans).
-// Measured on gfx950 for bfloat16 tiles, the transposing reads run at ~210 B/clk per CU when the
-// pitch is 64 bytes modulo 128 and at ~155 B/clk at every other 16-byte-aligned pitch tried (while
-// 16-byte reads of 32 consecutive rows then drop to ~80 B/clk, so tiles read both ways keep
-// lds_pitch).  float32 tiles are read with plain 4-byte reads and keep lds_pitch.
+// LDS row pitch (in elements) of a tile that is only read with transposing reads (frag_trans):
+// lds::padded_pitch_tr for bfloat16; float32 tiles are read with plain 4-byte reads and keep
+// lds_pitch.
 template <typename T, int DP>
 constexpr int lds_pitch_tr() {
   if constexpr (sizeof(T) != 2) {
     return lds_pitch<T, DP>();
   } else {
-    int bytes = DP * (int)sizeof(T);
-    while (bytes % 128 != 64) bytes += 16;
-    return bytes / (int)sizeof(T);
+    return lds::padded_pitch_tr(DP * (int)sizeof(T)) / (int)sizeof(T);
   }
 }
+
+// A staged tile of rows of D values of T that is read both as 32-row operands and transposed (the
+// Q and dO tiles of the dK/dV kernel, the K and V tiles of the dQ kernel): the layout lds::kind_for
+// picks (skewed rows for bfloat16 at d = 64 and 128, where both read forms are conflict-free;
+// padded rows, lds_pitch, otherwise).
+template <typename T, int D>
+struct StageTile {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KIND = lds::kind_for((int)sizeof(T), D);
+  static constexpr int RB = KIND != lds::kPadded ? lds::row_bytes_for(D) : lds_pitch<T, DP>() * (int)sizeof(T);
+  static constexpr int LD = RB / (int)sizeof(T);  // row pitch in elements (padded layout)
+  static constexpr int bytes(int rows) { return lds::tile_bytes(KIND, RB, rows); }
+  __device__ __forceinline__ static int offset(int row, int byte) { return lds::offset(KIND, RB, row, byte); }
+  __device__ __forceinline__ static int block(int row0) { return lds::block(KIND, RB, row0); }
+};
+
+// A staged tile that is only read transposed (the forward's V tiles): bfloat16 at d = 64 in the
+// lds::kSkewTr layout (conflict-free, no larger than padded rows), padded at lds_pitch_tr above
+// d = 64 (conflict-free), and at lds_pitch below.
+template <typename T, int D>
+struct TransTile {
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int KIND = sizeof(T) == 2 && D == 64 ? lds::kSkewTr : lds::kPadded;
+  static constexpr int RB = KIND != lds::kPadded ? 128
+                            : (DP > 64 ? lds_pitch_tr<T, DP>() : lds_pitch<T, DP>()) * (int)sizeof(T);
+  static constexpr int LD = RB / (int)sizeof(T);
+  static constexpr int bytes(int rows) { return lds::tile_bytes(KIND, RB, rows); }
+  __device__ __forceinline__ static int offset(int row, int byte) { return lds::offset(KIND, RB, row, byte); }
+  __device__ __forceinline__ static int block(int row0) { return lds::block(KIND, RB, row0); }
+};
+
+// Operand reads from StageTile / TransTile tiles (S).  In the skewed layouts each lane's offsets
+// within a 16-row-aligned block depend only on the lane, so they are computed once (one register
+// per read form) and every read is a register plus an immediate; padded tiles use the plain reads.
+template <typename T, class S>
+struct TileReader {
+  using M = Mfma<T>;
+  static constexpr bool SKEW = S::KIND != lds::kPadded;
+  // The second transposing read of a fragment is 8 rows below the first, at a lane-independent
+  // distance (rows 0-7 and 8-15 of a group differ by the same shift).
+  static constexpr int TR1 = lds::offset(S::KIND, S::RB, 8, 0) - lds::offset(S::KIND, S::RB, 0, 0);
+  int dir = 0, tr0 = 0;
+  __device__ __forceinline__ TileReader() {
+    if constexpr (SKEW) {
+      const int l = lane_id();
+      if constexpr (S::KIND == lds::kSkewed) dir = S::offset(lds::direct_row(l), lds::direct_byte(l, 0));
+      tr0 = S::offset(lds::trans_row(l, 0, 0), lds::trans_byte(l, 0));
+    }
+  }
+  // 32 x KSTEP operand of tile rows row0 .. row0 + 31 (row0 a multiple of 16), reduction step ks.
+  __device__ __forceinline__ typename M::frag direct(const lds_t* tile, int row0, int ks) const {
+    static_assert(S::KIND != lds::kSkewTr, "transposing reads only");
+    if constexpr (SKEW) return M::frag_at(tile + S::block(row0) + dir + 2 * ks * M::KSTEP);
+    else return M::frag_direct(tile, S::LD, row0 * S::LD + ks * M::KSTEP);
+  }
+  // Transposed operand of the 32-row block at row0 (a multiple of 16), columns 32 db .., instruction c.
+  __device__ __forceinline__ typename M::frag trans(const lds_t* tile, int row0, int db, int c) const {
+    if constexpr (SKEW) {
+      const lds_t* b = tile + S::block(row0 + 16 * c) + 64 * db + tr0;
+      return M::frag_tr_at(b, b + TR1);
+    } else {
+      return M::frag_trans(tile, S::LD, row0 * S::LD + db * 32, c);
+    }
+  }
+};
+template <typename T, int D>
+using StageReader = TileReader<T, StageTile<T, D>>;
 
 // Exchange a value with the lane 32 positions away (lanes l and l ^ 32 hold the two halves of
 // an accumulator column).
@@ -201,9 +264,21 @@ struct TileCopy {
     for (int i = 0; i < PER_THREAD; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       if (CHUNKS % NTHREADS == 0 || c < CHUNKS) {
-        const int row = c / CPR, cc = c % CPR;
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tile + (row * LD) * (int)sizeof(T) + cc * 16) = r[i];
+        const int row = lds::store_row(c, CPR);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tile + (row * LD) * (int)sizeof(T) +
+                                                                    lds::store_byte(c, CPR)) = r[i];
       }
+    }
+  }
+  // Store into a tile laid out as S (a StageTile).
+  template <class S>
+  __device__ __forceinline__ void store_to(lds_t* tile) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = threadIdx.x + i * NTHREADS;
+      if (CHUNKS % NTHREADS == 0 || c < CHUNKS)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+            tile + S::offset(lds::store_row(c, CPR), lds::store_byte(c, CPR))) = r[i];
     }
   }
 };
@@ -242,6 +317,18 @@ __device__ __forceinline__ void zero_pad_cols(lds_t* tile) {
     for (int i = threadIdx.x; i < ROWS * W; i += NTHREADS) {
       const int row = i / W, col = COLS + i % W;
       *reinterpret_cast<__attribute__((address_space(3))) T*>(tile + (row * LD + col) * (int)sizeof(T)) = T(0);
+    }
+  }
+}
+
+// zero_pad_cols for a tile laid out as S (a StageTile): columns [D, DP) of ROWS rows.
+template <class S, typename T, int ROWS, int D, int NTHREADS>
+__device__ __forceinline__ void zero_pad_stage(lds_t* tile) {
+  if constexpr (S::DP > D) {
+    constexpr int W = S::DP - D;
+    for (int i = threadIdx.x; i < ROWS * W; i += NTHREADS) {
+      const int row = i / W, col = D + i % W;
+      *reinterpret_cast<__attribute__((address_space(3))) T*>(tile + S::offset(row, col * (int)sizeof(T))) = T(0);
     }
   }
 }

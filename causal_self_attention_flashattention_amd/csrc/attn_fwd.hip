@@ -65,9 +65,10 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   constexpr int LD = lds_pitch<T, DP>();     // LDS row stride of K tiles (elements)
   // ... of V tiles, which are only read transposed (up to d = 64 the larger pitch would cost a
   // workgroup per CU: four of them fill the LDS with the K pitch)
-  constexpr int LDV = DP > 64 ? lds_pitch_tr<T, DP>() : LD;
-  constexpr int TILE = BKT * LD * (int)sizeof(T);    // bytes of one K tile
-  constexpr int TILEV = BKT * LDV * (int)sizeof(T);  // bytes of one V tile
+  // V tiles are only read transposed (TransTile: conflict-free for those reads).
+  using SV = TransTile<T, D>;
+  constexpr int TILE = BKT * LD * (int)sizeof(T);  // bytes of one K tile
+  constexpr int TILEV = SV::bytes(BKT);            // bytes of one V tile
   constexpr int STG = TILE + TILEV;                  // bytes of one stage (K tile, then V tile)
   constexpr int SHIFT = BK == 64 ? 0 : 1;          // key tiles per mask block = 1 << SHIFT
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   bool first = true;  // no tile run yet: the running max starts from the first tile's max
 
   if constexpr (DP > D) {
-    zero_pad_cols<T, BKT, D, LDV, DP, NT>(lds + TILE);
-    zero_pad_cols<T, BKT, D, LDV, DP, NT>(lds + STG + TILE);
+    zero_pad_stage<SV, T, BKT, D, NT>(lds + TILE);
+    zero_pad_stage<SV, T, BKT, D, NT>(lds + STG + TILE);
   }
   // Key tiles in loop order: all of [0, nkt), or (block-sparse) those some row of this workgroup
   // may see; the current, next and next-but-one tiles are tracked for the two-stage pipeline.
@@ -154,7 +155,9 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   }
   auto after = [&](int t) { return BSP ? next_live_tile(map, t + 1, t_hi, SHIFT) : t + 1; };
   TileCopy<T, BKT, D, LD, NT> kc;
-  TileCopy<T, BKT, D, LDV, NT> vc;
+  TileCopy<T, BKT, D, SV::LD, NT> vc;
+  auto store_v = [&](lds_t* dst) { vc.template store_to<SV>(dst); };
+  const TileReader<T, SV> vr;
   if (cur < t_hi) {
     kc.load(rk, cur * BKT);
     vc.load(rv, cur * BKT);
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   }
   if (cur < t_hi) {
     kc.store(lds);
-    vc.store(lds + TILE);
+    store_v(lds + TILE);
   }
   __syncthreads();
   if constexpr (STQ) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
       if (nxt < t_hi) {
         lds_t* st = lds + ((it + 1) & 1) * STG;
         kc.store(st);
-        vc.store(st + TILE);
+        store_v(st + TILE);
       }
       if (nxt2 < t_hi) {
         kc.load(rk, nxt2 * BKT);
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     }
     // This group's keys of the tile: rows grp * BK .. grp * BK + BK - 1 of the staged K and V.
     const lds_t* ktile = lds + (it & 1) * STG + grp * BK * LD * (int)sizeof(T);
-    const lds_t* vtile = lds + (it & 1) * STG + TILE + grp * BK * LDV * (int)sizeof(T);
+    const lds_t* vtile = lds + (it & 1) * STG + TILE + SV::block(grp * BK);
     const int k0 = cur * BKT + grp * BK;
     // (k0 is a multiple of 64 and qw of 32, so a wave that runs has key k0 visible in every row.)
     bool run = wave_live && k0 < kend && !(causal && k0 > qw_last);
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
         for (int c = 0; c < M::CALLS32; ++c)
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            o[db] = M::mma(M::frag_trans(vtile, LDV, nb * 32 * LDV + db * 32, c), pf[c], o[db]);
+            o[db] = M::mma(vr.trans(vtile, nb * 32, db, c), pf[c], o[db]);
       }
     }
     if constexpr (EARLY) {
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
       if (nxt < t_hi) {
         lds_t* st = lds + ((it + 1) & 1) * STG;
         kc.store(st);
-        vc.store(st + TILE);
+        store_v(st + TILE);
       }
       __syncthreads();
       if (nxt2 < t_hi) {
@@ -467,13 +470,16 @@ static hipError_t launch_fwd_t(const Problem& p, const void* Q, const void* K, c
   const float sl2 = p.scale * kLog2e;
   const int BH = p.B * p.H;
   if (nsplit > 1) {
+    // Split grids are small (a few workgroups per CU at most): at most two workgroups per CU are
+    // asked for, which leaves the register budget of the d = 64 kernel room to avoid spills.
+    constexpr int OCCS = OCC > 2 ? 2 : OCC;
     const int grid = BH * TQ * nsplit;
     if (p.bmask)
-      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, true, true>), dim3(grid), dim3(NW * 64), 0, stream,
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCCS, true, true>), dim3(grid), dim3(NW * 64), 0, stream,
                          (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
                          p.bmask, nsplit, part);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCC, false, true>), dim3(grid), dim3(NW * 64), 0, stream,
+      hipLaunchKernelGGL((fwd_kernel<T, D, NW, BK, OCCS, false, true>), dim3(grid), dim3(NW * 64), 0, stream,
                          (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, BH, p.H, p.N, p.causal, sl2, p.kv_len,
                          nullptr, nsplit, part);
     const hipError_t e = hipGetLastError();
