@@ -157,8 +157,8 @@ constexpr int lds_pitch_tr() {
 template <typename T, int D>
 struct StageTile {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int KIND = lds::kind_for((int)sizeof(T), D);
-  static constexpr int RB = KIND != lds::kPadded ? lds::row_bytes_for(D) : lds_pitch<T, DP>() * (int)sizeof(T);
+  static constexpr int KIND = lds::stage_kind((int)sizeof(T), D);
+  static constexpr int RB = lds::stage_row_bytes((int)sizeof(T), D);
   static constexpr int LD = RB / (int)sizeof(T);  // row pitch in elements (padded layout)
   static constexpr int bytes(int rows) { return lds::tile_bytes(KIND, RB, rows); }
   __device__ __forceinline__ static int offset(int row, int byte) { return lds::offset(KIND, RB, row, byte); }
@@ -171,9 +171,8 @@ struct StageTile {
 template <typename T, int D>
 struct TransTile {
   static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int KIND = sizeof(T) == 2 && D == 64 ? lds::kSkewTr : lds::kPadded;
-  static constexpr int RB = KIND != lds::kPadded ? 128
-                            : (DP > 64 ? lds_pitch_tr<T, DP>() : lds_pitch<T, DP>()) * (int)sizeof(T);
+  static constexpr int KIND = lds::trans_kind((int)sizeof(T), D);
+  static constexpr int RB = lds::trans_row_bytes((int)sizeof(T), D);
   static constexpr int LD = RB / (int)sizeof(T);
   static constexpr int bytes(int rows) { return lds::tile_bytes(KIND, RB, rows); }
   __device__ __forceinline__ static int offset(int row, int byte) { return lds::offset(KIND, RB, row, byte); }

@@ -79,6 +79,24 @@ ATTN_HD constexpr int skew(int rb, int r) {
 }
 ATTN_HD constexpr int skew_group_bytes(int rb) { return rb == 256 ? 4928 : rb == 192 ? 3136 : 2368; }
 
+// The kernels' tiles, by element size and head dim d (dp = d rounded up to 32 columns):
+//  * stage tiles, read both ways (dK/dV's Q and dO, dQ's K and V): skewed where kind_for says so,
+//    else padded at padded_pitch;
+//  * forward K tiles (32-row operand reads only): padded at padded_pitch;
+//  * forward V tiles (transposing reads only): kSkewTr for bfloat16 at d = 64, padded at
+//    padded_pitch_tr above d = 64, padded at padded_pitch below.
+ATTN_HD constexpr int dp_for(int d) { return (d + 31) / 32 * 32; }
+ATTN_HD constexpr int stage_kind(int elem_bytes, int d) { return kind_for(elem_bytes, d); }
+ATTN_HD constexpr int stage_row_bytes(int elem_bytes, int d) {
+  return kind_for(elem_bytes, d) != kPadded ? row_bytes_for(d) : padded_pitch(dp_for(d) * elem_bytes);
+}
+ATTN_HD constexpr int trans_kind(int elem_bytes, int d) { return elem_bytes == 2 && d == 64 ? kSkewTr : kPadded; }
+ATTN_HD constexpr int trans_row_bytes(int elem_bytes, int d) {
+  return trans_kind(elem_bytes, d) != kPadded ? 128
+         : dp_for(d) > 64 && elem_bytes == 2 ? padded_pitch_tr(dp_for(d) * elem_bytes)
+                                             : padded_pitch(dp_for(d) * elem_bytes);
+}
+
 // Transposing reads only, 128-byte rows: rows 4a .. 4a + 3 start at 16-byte slots 0, 8, 4, 12 plus
 // 4a modulo 16, so the 4 chunks 4u .. 4u + 3 of the 4 rows fill 16 different slots: (b).
 ATTN_HD constexpr int skew_tr(int r) { return 64 * ((r >> 2) + ((r >> 1) & 1)); }
