@@ -345,9 +345,8 @@ __device__ __forceinline__ void settle(const F& f) { asm volatile("" ::"v"(f)); 
 // keys, the key tiles that see the most queries), so the heavy items of all heads start first and
 // the light ones fill in at the end instead of a late head's heaviest tile setting the time.  The
 // 8 XCDs receive blocks round-robin: with nheads a multiple of 8 every item of a head lands on one
-// XCD and shares the head's K/V in that XCD's L2; otherwise a head's items alternate between a
-// few XCDs, which keeps the XCDs evenly loaded (padding the heads to a multiple of 8 slots kept
-// locality but loaded the XCDs unevenly: 9% slower at 36 heads).  Blocks past the last item get -1.
+// XCD and shares the head's K/V in that XCD's L2; otherwise xcd_block below keeps the heads on as
+// few XCDs as the balance allows.  Blocks past the last item get -1.
 __device__ __forceinline__ int rank_major_block(int nheads, int nranks, int b) {
   if (b >= nheads * nranks) return -1;
   return (b % nheads) * nranks + b / nheads;
@@ -361,7 +360,9 @@ __device__ __forceinline__ int rank_major_block(int nheads, int nranks, int b) {
 // head j goes to the 8 / hr XCDs j (8 / hr) + (r mod 8 / hr) (so each is split over that many),
 // otherwise rank r of remaining head j goes to XCD (r + j) mod 8.  Every XCD then holds the same
 // number of items of the same mix of ranks (balanced causal work), and runs them rank-major,
-// heaviest first.  Needs nranks to be a multiple of the period of that split; otherwise, and when
+// heaviest first.  (Running an XCD's heads one after another instead cuts the L2 misses further
+// but starts heavy items late: 8% slower at 36 heads, 14% at 80.)  Needs nranks to be a multiple
+// of the period of that split; otherwise, and when
 // nheads is a multiple of 8 (where rank-major order already keeps each head on one XCD), it is
 // rank_major_block.  A bijection from [0, nheads nranks) onto the items.
 __device__ __forceinline__ int xcd_block(int nheads, int nranks, int b) {

@@ -62,14 +62,13 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;             // key blocks per wave and tile
   constexpr int BKT = G * BK;             // keys per tile
-  constexpr int LD = lds_pitch<T, DP>();     // LDS row stride of K tiles (elements)
-  // ... of V tiles, which are only read transposed (up to d = 64 the larger pitch would cost a
-  // workgroup per CU: four of them fill the LDS with the K pitch)
-  // V tiles are only read transposed (TransTile: conflict-free for those reads).
+  // K tiles are only read as 32-row operands (padded rows at lds_pitch, conflict-free for those
+  // reads); V tiles only transposed (TransTile, conflict-free for those).
+  constexpr int LD = lds_pitch<T, DP>();           // LDS row stride of K tiles (elements)
   using SV = TransTile<T, D>;
   constexpr int TILE = BKT * LD * (int)sizeof(T);  // bytes of one K tile
   constexpr int TILEV = SV::bytes(BKT);            // bytes of one V tile
-  constexpr int STG = TILE + TILEV;                  // bytes of one stage (K tile, then V tile)
+  constexpr int STG = TILE + TILEV;                // bytes of one stage (K tile, then V tile)
   constexpr int SHIFT = BK == 64 ? 0 : 1;          // key tiles per mask block = 1 << SHIFT
   static_assert(D % M::KSTEP == 0, "head dim must be a multiple of the MFMA reduction depth");
   static_assert(!BSP || (QT % kMaskBlock == 0 && QT / kMaskBlock <= 8 && (BK == 32 || BK == 64)),
