@@ -7,9 +7,10 @@
 // 16p .. 16p + 15) and is conflict-free when those lanes' 16-byte chunks fall in distinct 16-byte
 // slots modulo 256 bytes.  A transposing 8-byte read (ds_read_b64_tr_b16) is served 32 lanes at a
 // time and is conflict-free when those lanes' 8-byte words fall in distinct 8-byte slots modulo
-// 256 bytes.  A conflict of degree k costs k - 1 extra cycles per pass.
+// 256 bytes.  A 16-byte store is served 8 lanes at a time, with 16-byte chunks modulo 128 bytes.
+// A conflict of degree k costs k - 1 extra cycles per pass.
 //
-// Tiles hold rows of bfloat16 (or float32) values.  Two layouts:
+// Tiles hold rows of bfloat16 (or float32) values.  Three layouts:
 //  * padded: row r at r * P bytes, P = the row's data bytes plus padding (lds_pitch,
 //    lds_pitch_tr);
 //  * skewed: rows of RB = 128 or 256 bytes in groups of 16, row r of a group shifted by a function
@@ -19,7 +20,8 @@
 //    bytes (144 bytes per row on average, as the padded pitch of such rows).
 // A tile read both as 32-row operands (16 bytes per lane) and transposed can be conflict-free for
 // both only in the skewed layout: no padded pitch is (a pitch that is an odd number of 16-byte
-// chunks suits the first, one that is 64 bytes modulo 128 the second).
+// chunks suits the first, one that is 64 bytes modulo 128 the second).  Row-contiguous stores are
+// conflict-free in every layout whose rows are a multiple of 128 data bytes.
 #pragma once
 
 #if defined(__HIPCC__)
