@@ -44,7 +44,7 @@ DEFAULT_WORKLOAD = "10b-16k"
 SECONDARY_WORKLOADS = ("large-4k",)
 KERNELS_SPLIT = ("fwd", "dq", "dkdv")  # launch order of one step when attn_bwd launches two kernels
 KERNELS_FUSED = ("fwd", "bwd")        # ... and when its dQ and dK/dV work share one launch
-KERNEL_SOURCES = ("attn_device.h", "lds_layout.h", "attn_fwd.hip", "attn_bwd.hip")
+KERNEL_SOURCES = ("attn_device.h", "block_order.h", "lds_layout.h", "attn_fwd.hip", "attn_bwd.hip")
 
 
 def npairs(N: int, kv: int, causal: bool) -> int:

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "block_order.h"
 #include "lds_layout.h"
 
 namespace attn {
@@ -338,58 +339,6 @@ __device__ __forceinline__ void zero_pad_stage(lds_t* tile) {
 // latency per iteration.
 template <typename F>
 __device__ __forceinline__ void settle(const F& f) { asm volatile("" ::"v"(f)); }
-
-// Block index -> logical work item h * nranks + r (head h, rank r), rank-major: blocks
-// 0 .. nheads-1 take rank 0 of every head, the next nheads blocks rank 1, and so on.  Callers
-// number a head's items heaviest first (under causal masking, the query tiles that see the most
-// keys, the key tiles that see the most queries), so the heavy items of all heads start first and
-// the light ones fill in at the end instead of a late head's heaviest tile setting the time.  The
-// 8 XCDs receive blocks round-robin: with nheads a multiple of 8 every item of a head lands on one
-// XCD and shares the head's K/V in that XCD's L2; otherwise xcd_block below keeps the heads on as
-// few XCDs as the balance allows.  Blocks past the last item get -1.
-__device__ __forceinline__ int rank_major_block(int nheads, int nranks, int b) {
-  if (b >= nheads * nranks) return -1;
-  return (b % nheads) * nranks + b / nheads;
-}
-
-// Block index -> logical work item (as rank_major_block) with each head's items kept on one XCD
-// where that can be balanced.  The 8 XCDs receive blocks round-robin (block b runs on XCD b % 8,
-// in order b / 8 there), and each XCD has its own L2: the items of a head that share its K and V
-// rows should run on one XCD.  With nheads = 8 hq + hr (0 < hr), XCD x takes whole heads
-// x hq .. x hq + hq - 1 and a share of the hr remaining heads by rank: when hr divides 8, remaining
-// head j goes to the 8 / hr XCDs j (8 / hr) + (r mod 8 / hr) (so each is split over that many),
-// otherwise rank r of remaining head j goes to XCD (r + j) mod 8.  Every XCD then holds the same
-// number of items of the same mix of ranks (balanced causal work), and runs them rank-major,
-// heaviest first.  (Running an XCD's heads one after another instead cuts the L2 misses further
-// but starts heavy items late: 8% slower at 36 heads, 14% at 80.)  Needs nranks to be a multiple
-// of the period of that split; otherwise, and when
-// nheads is a multiple of 8 (where rank-major order already keeps each head on one XCD), it is
-// rank_major_block.  A bijection from [0, nheads nranks) onto the items.
-__device__ __forceinline__ int xcd_block(int nheads, int nranks, int b) {
-  constexpr int NX = 8;
-  const int hq = nheads / NX, hr = nheads % NX;
-  const bool divides = hr > 0 && NX % hr == 0;
-  const int T = divides ? NX / hr : NX;  // ranks per period of the split
-  if (hr == 0 || nranks % T != 0 || b >= nheads * nranks) return rank_major_block(nheads, nranks, b);
-  const int x = b % NX, i = b / NX;
-  const int P = T * hq + (divides ? 1 : hr);  // items of XCD x per period
-  const int p = i / P;
-  int q = i % P;
-  for (int rp = 0; rp < T; ++rp) {
-    const int r = p * T + rp;
-    int j;  // remaining head that XCD x serves at rank r, or -1
-    if (divides) {
-      j = (r % T == x % T) ? x / T : -1;
-    } else {
-      j = ((x - r) % NX + NX) % NX;
-      if (j >= hr) j = -1;
-    }
-    const int n = hq + (j >= 0 ? 1 : 0);
-    if (q < n) return (q < hq ? x * hq + q : NX * hq + j) * nranks + r;
-    q -= n;
-  }
-  return -1;  // not reached: the P items of a period are enumerated above
-}
 
 // ------------------------------------------------------------------------------------------
 // Block-sparse masks.  A mask is uint8 [TB][TB], TB = ceil(N / kMaskBlock), row-major, shared by
