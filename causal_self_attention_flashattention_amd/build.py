@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_noalloc.hip", "attn_api.cpp"]
 MICROBENCH = os.path.join(PKG, "microbench")
-MICROBENCH_SOURCES = ["lds_banks.hip", "mfma_rate.hip"]
+MICROBENCH_SOURCES = ["lds_banks.hip", "mfma_rate.hip", "valu_rate.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

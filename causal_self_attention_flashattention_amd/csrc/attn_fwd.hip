@@ -35,6 +35,15 @@ constexpr bool kStoreEarly = ATTN_STORE_EARLY;
 #define ATTN_XCD_MAP 1
 #endif
 constexpr bool kXcdMap = ATTN_XCD_MAP;
+#ifndef ATTN_PIPELINE
+#define ATTN_PIPELINE 1
+#endif
+constexpr bool kPipeline = ATTN_PIPELINE;
+
+template <int V>
+struct Flag {
+  static constexpr int value = V;
+};
 
 // With SPLIT the key range of every query tile is cut into `nsplit` chunks, one workgroup each;
 // a workgroup then writes its unnormalised O rows and their (running max, row sum) to `part`
@@ -157,30 +166,170 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   TileCopy<T, BKT, D, SV::LD, NT> vc;
   auto store_v = [&](lds_t* dst) { vc.template store_to<SV>(dst); };
   const TileReader<T, SV> vr;
-  if (cur < t_hi) {
-    kc.load(rk, cur * BKT);
-    vc.load(rv, cur * BKT);
-  }
-  // The Q fragments (or rows) were requested first: waiting for them here leaves the first K/V
-  // tile's loads in flight, so the two memory latencies overlap.
-  if constexpr (STQ) {
-    qst.store(lds + STG);
-  } else {
+
+  // Software-pipelined tiles (bf16, d = 128, dense, unsplit).  The key tiles [0, tp) that no mask
+  // touches (every key below the workgroup's first query and below the key length) run with three
+  // tiles in flight per straight-line iteration: iteration j forms the scores of tile j + 1, the
+  // softmax of tile j (scores from the previous iteration) and the P V product of tile j - 1
+  // (weights from the previous iteration).  The three parts are independent, so one wave can
+  // issue the vector work of a softmax while its own matrix products run.  K runs one tile ahead
+  // of V: iteration j writes K(j + 2) and V(j) into stage j & 1 and reads K(j + 1) and V(j - 1)
+  // from stage (j + 1) & 1; the barrier ending an iteration publishes its writes and retires its
+  // reads.  O is rescaled for tile j's max after tile j - 1's product, so every value is computed
+  // in the same order as in the plain loop below, which takes over at tile tp.
+  constexpr bool PIPE = kPipeline && sizeof(T) == 2 && D == 128 && G == 1 && !BSP && !SPLIT;
+  int it0 = 0;        // stage parity of the plain loop's first iteration
+  bool piped = false;  // the plain loop starts with its first tile staged and the next one loaded
+  if constexpr (PIPE) {
+    const int tp = min(causal ? q0 / BKT : nkt, kv / BKT);
+    if (tp >= 2) {
+      piped = true;
+      // Two register sets, used alternately by even and odd iterations (unrolled by two, so every
+      // index is static): scores of the current / next tile, weights of the current / previous.
+      f32x16 sa[2][NB];
+      typename M::frag pa[2][NB][M::CALLS32];
+      auto scores_at = [&](const lds_t* kt, f32x16* s) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
-  }
-  if (cur < t_hi) {
-    kc.store(lds);
-    store_v(lds + TILE);
-  }
-  __syncthreads();
-  if constexpr (STQ) {
+        for (int nb = 0; nb < NB; ++nb) {
+          s[nb] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = M::frag_direct(lds + STG, LD, 32 * w * LD + ks * M::KSTEP);
-    __syncthreads();  // every wave holds its fragments before the first iteration refills the slot
+          for (int ks = 0; ks < KS; ++ks)
+            s[nb] = M::mma(M::frag_direct(kt, LD, nb * 32 * LD + ks * M::KSTEP), qf[ks], s[nb]);
+        }
+      };
+      auto pv_at = [&](const lds_t* vt, const typename M::frag (*pp)[M::CALLS32]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int c = 0; c < M::CALLS32; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = M::mma(vr.trans(vt, nb * 32, db, c), pp[nb][c], o[db]);
+      };
+      // Iteration j (par = j & 1: the loop is unrolled by two, so the register set and the stage
+      // each iteration uses are static).
+      auto step = [&](int j, auto has_prev, auto has_next, auto par) {
+        constexpr int P = decltype(par)::value;
+        f32x16* sc = sa[P];
+        f32x16* sn = sa[P ^ 1];
+        typename M::frag(*pc)[M::CALLS32] = pa[P];
+        lds_t* wr = lds + P * STG;
+        const lds_t* rd = lds + (P ^ 1) * STG;
+        kc.store(wr);        // K(j + 2)
+        store_v(wr + TILE);  // V(j)
+        kc.load(rk, min(j + 3, tp + 1) * BKT);
+        vc.load(rv, (j + 1) * BKT);
+        if constexpr (decltype(has_next)::value) scores_at(rd, sn);
+        // Softmax of tile j: row max, the running max moved when exceeded by more than the slack.
+        float mx = sc[0][0];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int e = (nb == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, sc[nb][e]);
+        mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+        const bool need = mx > m_run + kRescaleSlack;
+        const float alpha = fast_exp2(m_run - mx);
+        l_part = need ? l_part * alpha : l_part;
+        m_run = need ? mx : m_run;
+        const float neg_m = -m_run;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sc[nb][e] = fast_exp2(__builtin_fmaf(sc[nb][e], scale_log2, neg_m));
+          float lsum = 0.f;
+#pragma unroll
+          for (int c = 0; c < M::CALLS32; ++c) {
+            pc[nb][c] = M::acc_frag(sc[nb], c);
+            lsum = M::frag_sum(pc[nb][c], lsum);
+          }
+          l_part += lsum;
+        }
+        if constexpr (decltype(has_prev)::value) pv_at(rd + TILE, pa[P ^ 1]);
+        // The weights are formed before the rescale branch, so their vector work shares a block
+        // with the products.  (The row sums are left to the compiler, which places their dot2s
+        // after it: beside busy matrix cores a dot2 costs several times a plain add.)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int c = 0; c < M::CALLS32; ++c) settle(pc[nb][c]);
+        if (need) {
+#pragma unroll
+          for (int i = 0; i < NDB; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        }
+        __syncthreads();
+      };
+      // Prologue: K(0) and K(1) staged, V(0) and K(2) in registers, tile 0's scores formed.
+      TileCopy<T, BKT, D, LD, NT> kc2;
+      kc.load(rk, 0);
+      kc2.load(rk, BKT);
+      vc.load(rv, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+      kc.store(lds);
+      kc2.store(lds + STG);
+      kc.load(rk, 2 * BKT);
+      __syncthreads();
+      scores_at(lds, sa[0]);
+      __syncthreads();  // stage 0's K slot is rewritten by iteration 0
+      const Flag<1> yes;
+      const Flag<0> no;
+      // Tile tp - 1's product (its weights and V(tp - 1) in register set / stage P = (tp - 1) & 1);
+      // V(tp) completes stage tp & 1 for the plain loop, which finds the next tile (K(tp + 1),
+      // V(tp + 1)) in registers.
+      auto drain = [&](auto par) {
+        constexpr int P = decltype(par)::value;
+        store_v(lds + (P ^ 1) * STG + TILE);
+        vc.load(rv, (tp + 1) * BKT);
+        pv_at(lds + P * STG + TILE, pa[P]);
+        __syncthreads();
+      };
+      step(0, no, yes, no);
+      int j = 1;
+      for (; j + 2 < tp; j += 2) {
+        step(j, yes, yes, yes);
+        step(j + 1, yes, yes, no);
+      }
+      if (j == tp - 1) {
+        step(j, yes, no, yes);
+        drain(yes);
+      } else {
+        step(j, yes, yes, yes);
+        step(j + 1, yes, no, no);
+        drain(no);
+      }
+      cur = tp;
+      it0 = tp;
+      first = false;
+    }
+  }
+
+  if (!piped) {
+    if (cur < t_hi) {
+      kc.load(rk, cur * BKT);
+      vc.load(rv, cur * BKT);
+    }
+    // The Q fragments (or rows) were requested first: waiting for them here leaves the first K/V
+    // tile's loads in flight, so the two memory latencies overlap.
+    if constexpr (STQ) {
+      qst.store(lds + STG);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
+    }
+    if (cur < t_hi) {
+      kc.store(lds);
+      store_v(lds + TILE);
+    }
+    __syncthreads();
+    if constexpr (STQ) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = M::frag_direct(lds + STG, LD, 32 * w * LD + ks * M::KSTEP);
+      __syncthreads();  // every wave holds its fragments before the first iteration refills the slot
+    }
   }
   int nxt = cur < t_hi ? after(cur) : t_hi;
-  if (nxt < t_hi) {
+  if (!piped && nxt < t_hi) {
     kc.load(rk, nxt * BKT);
     vc.load(rv, nxt * BKT);
   }
@@ -188,7 +337,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   // measured faster: the writes overlap the tile's products) or right before the barrier.
   constexpr bool EARLY = kStoreEarly && D > 80;
 
-  for (int it = 0; cur < t_hi; ++it) {
+  for (int it = it0; cur < t_hi; ++it) {
     int nxt2 = t_hi;
     if constexpr (EARLY) {
       // The next tile (loaded one iteration ago) goes to LDS at the start of the iteration, into
