@@ -88,6 +88,14 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 // LDS bytes of the dK/dV body: two stages of (Q tile, dO tile, L row, D row), then either (DSELF)
 // one float of D per query row for rows up to kDselfMaxN, or (VLDS) the workgroup's V rows.
 constexpr int kDselfMaxN = 4096;
+#ifndef ATTN_DQ_FULL
+#define ATTN_DQ_FULL 1
+#endif
+constexpr bool kDqFull = ATTN_DQ_FULL;
+#ifndef ATTN_DKDV_FULL
+#define ATTN_DKDV_FULL 1
+#endif
+constexpr bool kDkdvFull = ATTN_DKDV_FULL;
 template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, int G = 1>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
@@ -349,7 +357,60 @@ __device__ __forceinline__ void dkdv_body(
       const __attribute__((address_space(3))) float* drow = DSELF ? dself + (cur - qt0) * BQS : lrow + BQS;
       bool run = wave_live;
       if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
-      if (run) {
+      // A stage whose rows all see all of this wave's keys (no mask, every query block in range)
+      // runs its query blocks as one straight-line block: both blocks' score and dP products first,
+      // then each block's weights, dS and dV / dK products, so the second block's products can issue
+      // beside the first block's vector work.  Same arithmetic, in the same order per value.  Up to
+      // d = 64 only: above, the second block's accumulators do not fit the register file.
+      const bool full = kDkdvFull && D <= 64 && NQB > 1 && KB == 1 && G == 1 && q0 + BQS <= N &&
+                        kw + 32 <= kv && (!causal || kw + 31 <= q0);
+      if (run && full) {
+        f32x16 s[NQB], dp[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 dd = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(drow + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dp[qb][4 * m + r] = dd[r];
+          }
+          s[qb] = f32x16{};
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            s[qb] = M::mma(sr.direct(qtile, qb * 32, ks), kf[0][ks], s[qb]);
+            if constexpr (VLDS)
+              dp[qb] = M::mma(sr.direct(otile, qb * 32, ks), M::frag_direct(vt, LD, (w * KW) * LD + ks * M::KSTEP), dp[qb]);
+            else
+              dp[qb] = M::mma(sr.direct(otile, qb * 32, ks), vf[0][ks], dp[qb]);
+          }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lrow + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * m + r;
+              const float p = fast_exp2(__builtin_fmaf(s[qb][e], scale_log2, -lv[r]));
+              s[qb][e] = p;
+              dp[qb][e] = p * dp[qb][e];
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < M::CALLS32; ++c) {
+            const typename M::frag pf = M::acc_frag(s[qb], c);
+            const typename M::frag sf = M::acc_frag(dp[qb], c);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              dv[0][db] = M::mma(sr.trans(otile, qb * 32, db, c), pf, dv[0][db]);
+              dk[0][db] = M::mma(sr.trans(qtile, qb * 32, db, c), sf, dk[0][db]);
+            }
+          }
+        }
+      } else if (run) {
 #pragma unroll
         for (int qbw = 0; qbw < NQB; ++qbw) {
           const int qb = grp * NQB + qbw;  // query block within the stage
@@ -756,7 +817,43 @@ __device__ __forceinline__ void dq_body(
     const lds_t* vtile = ktile + TILE;
     bool run = wave_live;
     if constexpr (BSP) run = run && (tile_bits(map, cur, SHIFT) & wave_bit);
-    if (run) {
+    // A tile whose keys are all visible to all of this wave's queries (no mask, every key block
+    // in range) runs its key blocks as one straight-line block: both blocks' score and dP products
+    // first, then each block's weights, dS and dQ products, so the second block's products can
+    // issue beside the first block's vector work.  Same arithmetic, in the same order per value.
+    const int kt0 = cur * BKT + grp * BK;
+    const bool full = kDqFull && NB > 1 && kt0 + BK <= kend && (!causal || kt0 + BK - 1 <= qw);
+    if (run && full) {
+      f32x16 s[NB], dp[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb] = f32x16{};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[nb][e] = D > 80 ? -dq_ : 0.f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[nb] = M::mma(sr.direct(ktile, nb * 32, ks), qf[ks], s[nb]);
+          dp[nb] = M::mma(sr.direct(vtile, nb * 32, ks), of[ks], dp[nb]);
+        }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, -lq));
+          dp[nb][e] = D > 80 ? p * dp[nb][e] : p * (dp[nb][e] - dq_);
+        }
+#pragma unroll
+        for (int c = 0; c < M::CALLS32; ++c) {
+          const typename M::frag sf = M::acc_frag(dp[nb], c);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf, acc[db]);
+        }
+      }
+    } else if (run) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int kb0 = cur * BKT + grp * BK + nb * 32;
