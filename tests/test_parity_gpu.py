@@ -56,6 +56,10 @@ SMALL += [
     ("bf16", 3, 3, 1024, 128, True, [1024, 900, 700]),
     ("bf16", 1, 6, 1024, 80, True, None),
     ("bf16", 2, 1, 1024, 64, True, None),
+    # the d = 128 forward's pipelined loop (grids above the two-group threshold) ending at the key
+    # length rather than the diagonal, without causal masking, and with a partial last query tile
+    ("bf16", 2, 24, 1024, 128, False, [1000, 777]),
+    ("bf16", 2, 18, 1100, 128, True, [1100, 900]),
 ]
 
 
