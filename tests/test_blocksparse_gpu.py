@@ -87,7 +87,7 @@ def test_blocksparse_matches_oracle(B, H, N, d, dtype, causal, kv, density, head
 # another order).
 @pytest.mark.parametrize("N,d,dtype,causal,BH", [(300, 64, "bf16", True, 100), (257, 128, "f32", False, 2),
                                                   (1024, 64, "bf16", True, 40), (1024, 128, "bf16", True, 128),
-                                                  (1024, 128, "bf16", False, 64)])
+                                                  (1024, 128, "bf16", False, 64), (1024, 80, "bf16", True, 64)])
 def test_all_ones_mask_equals_dense_bitwise(N, d, dtype, causal, BH):
     inp = make_inputs(1, BH, N, d, dtype, seed=3)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))

@@ -60,6 +60,8 @@ SMALL += [
     # length rather than the diagonal, without causal masking, and with a partial last query tile
     ("bf16", 2, 24, 1024, 128, False, [1000, 777]),
     ("bf16", 2, 18, 1100, 128, True, [1100, 900]),
+    # d = 80 with one key group per workgroup, key padding, no causal mask
+    ("bf16", 2, 20, 1024, 80, False, [1000, 700]),
 ]
 
 
