@@ -104,6 +104,31 @@ template <> struct Mfma<__bf16> {
     if (valid) f = *reinterpret_cast<const frag*>(rowp + col0 + KPL * (lane_id() >> 5));
     return f;
   }
+
+  // 16-wide products for output blocks of 16 rows (the last 16 of a head dim that is 16 modulo 32),
+  // v_mfma_f32_16x16x32_bf16: A (16 x 32): lane l holds A[l % 16][8 (l / 16) + s]; B (32 x 16): lane
+  // l holds B[8 (l / 16) + s][l % 16]; accumulator (16 x 16): lane l, element e holds
+  // C[4 (l / 16) + e][l % 16].
+  __device__ __forceinline__ static f32x4 mma16(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // The two B operands of a 32-row accumulator block's weights (p0, p1: acc_frag c = 0, 1) for the
+  // 16-wide products over its 32 rows: `lo` for accumulator columns 0-15, `hi` for 16-31.  Lane
+  // group g = l / 16 of either holds the rows that acc_frag g % 2 holds in lane half g / 2, which
+  // one v_permlane16_swap per register moves into place (rows of 16 lanes: the odd rows of p0 trade
+  // places with the even rows of p1).
+  __device__ __forceinline__ static void tail_weights(const frag& p0, const frag& p1, frag& lo, frag& hi) {
+    const u32x4 a = __builtin_bit_cast(u32x4, p0), b = __builtin_bit_cast(u32x4, p1);
+    u32x4 x, y;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto r = __builtin_amdgcn_permlane16_swap(a[k], b[k], false, false);
+      x[k] = r[0];
+      y[k] = r[1];
+    }
+    lo = __builtin_bit_cast(frag, x);
+    hi = __builtin_bit_cast(frag, y);
+  }
 };
 
 template <> struct Mfma<float> {
@@ -167,8 +192,9 @@ struct StageTile {
 };
 
 // A staged tile that is only read transposed (the forward's V tiles): bfloat16 at d = 64 in the
-// lds::kSkewTr layout (conflict-free, no larger than padded rows), padded at lds_pitch_tr above
-// d = 64 (conflict-free), and at lds_pitch below.
+// lds::kSkewTr layout (conflict-free, no larger than padded rows), at d = 80 in lds::kShift16 rows
+// of lds_pitch_tr (the 32- and 16-column reads conflict-free), padded at lds_pitch_tr above d = 64
+// (conflict-free), and at lds_pitch below.
 template <typename T, int D>
 struct TransTile {
   static constexpr int DP = (D + 31) / 32 * 32;
@@ -190,17 +216,18 @@ struct TileReader {
   // The second transposing read of a fragment is 8 rows below the first, at a lane-independent
   // distance (rows 0-7 and 8-15 of a group differ by the same shift).
   static constexpr int TR1 = lds::offset(S::KIND, S::RB, 8, 0) - lds::offset(S::KIND, S::RB, 0, 0);
-  int dir = 0, tr0 = 0;
-  __device__ __forceinline__ TileReader() {
+  int dir = 0, tr0 = 0, t16 = 0;
+  __device__ __forceinline__ TileReader(bool with16 = false) {
+    const int l = lane_id();
     if constexpr (SKEW) {
-      const int l = lane_id();
       if constexpr (S::KIND == lds::kSkewed) dir = S::offset(lds::direct_row(l), lds::direct_byte(l, 0));
       tr0 = S::offset(lds::trans_row(l, 0, 0), lds::trans_byte(l, 0));
     }
+    if (with16) t16 = S::offset(lds::trans16_row(l, 0), lds::trans16_byte(l, 0));
   }
   // 32 x KSTEP operand of tile rows row0 .. row0 + 31 (row0 a multiple of 16), reduction step ks.
   __device__ __forceinline__ typename M::frag direct(const lds_t* tile, int row0, int ks) const {
-    static_assert(S::KIND != lds::kSkewTr, "transposing reads only");
+    static_assert(S::KIND != lds::kSkewTr && S::KIND != lds::kShift16, "transposing reads only");
     if constexpr (SKEW) return M::frag_at(tile + S::block(row0) + dir + 2 * ks * M::KSTEP);
     else return M::frag_direct(tile, S::LD, row0 * S::LD + ks * M::KSTEP);
   }
@@ -213,6 +240,13 @@ struct TileReader {
       return M::frag_trans(tile, S::LD, row0 * S::LD + db * 32, c);
     }
   }
+  // A operand of Mfma<__bf16>::mma16 over the 32-row block at row0 (a multiple of 32) and tile
+  // columns col0 .. col0 + 15, rows in the order of Mfma<__bf16>::tail_weights (the reader must be
+  // constructed with with16).
+  __device__ __forceinline__ typename M::frag trans16(const lds_t* tile, int row0, int col0) const {
+    const lds_t* b = tile + S::block(row0) + t16 + 2 * col0;
+    return M::frag_tr_at(b, b + TR1);
+  }
 };
 template <typename T, int D>
 using StageReader = TileReader<T, StageTile<T, D>>;
@@ -222,6 +256,14 @@ using StageReader = TileReader<T, StageTile<T, D>>;
 __device__ __forceinline__ float swap_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
+}
+
+// From a per-lane value of query (column) l % 32, the values of columns l % 16 (lo) and 16 + l % 16
+// (hi): the per-column factors of 16-wide accumulators.
+__device__ __forceinline__ void split16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -68,6 +68,11 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   constexpr int QT = 32 * NW;             // queries per workgroup
   constexpr int DP = (D + 31) / 32 * 32;  // head dim rounded up to a 32-row MFMA block
   constexpr int NDB = DP / 32;
+  // bf16 head dims of 16 modulo 32 (16, 80): the last 16 output columns run on 16-wide products
+  // (two 16 x 16 accumulators per wave, for its queries 0-15 and 16-31) instead of a 32-row block
+  // half of padding; NDA full 32-row blocks precede them.
+  constexpr bool T16 = sizeof(T) == 2 && DP - D == 16;
+  constexpr int NDA = T16 ? D / 32 : NDB;
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;             // key blocks per wave and tile
   constexpr int BKT = G * BK;             // keys per tile
@@ -143,13 +148,23 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     for (int ks = 0; ks < KS; ++ks) qf[ks] = frag_global<T>(rq, q, D, ks * M::KSTEP);
   }
 
-  f32x16 o[NDB];
+  f32x16 o[NDA > 0 ? NDA : 1];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  for (int i = 0; i < NDA; ++i) o[i] = f32x16{};
+  f32x4 ot[2] = {};  // T16: O^T columns 32 NDA .. D - 1 of queries 0-15 and 16-31
+  // Rescale the 16-wide accumulators by each query's factor (a: this lane's query's).
+  auto scale_tail = [&](float a) {
+    if constexpr (T16) {
+      float lo, hi;
+      split16(a, lo, hi);
+      ot[0] *= lo;
+      ot[1] *= hi;
+    }
+  };
   float m_run = -INFINITY, l_part = 0.f;
   bool first = true;  // no tile run yet: the running max starts from the first tile's max
 
-  if constexpr (DP > D) {
+  if constexpr (DP > D && !T16) {
     zero_pad_stage<SV, T, BKT, D, NT>(lds + TILE);
     zero_pad_stage<SV, T, BKT, D, NT>(lds + STG + TILE);
   }
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   TileCopy<T, BKT, D, LD, NT> kc;
   TileCopy<T, BKT, D, SV::LD, NT> vc;
   auto store_v = [&](lds_t* dst) { vc.template store_to<SV>(dst); };
-  const TileReader<T, SV> vr;
+  const TileReader<T, SV> vr(T16);
 
   // Software-pipelined tiles (bf16, d = 128, dense, unsplit).  The key tiles [0, tp) that no mask
   // touches (every key below the workgroup's first query and below the key length) run with three
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 #pragma unroll
           for (int c = 0; c < M::CALLS32; ++c)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = M::mma(vr.trans(vt, nb * 32, db, c), pp[nb][c], o[db]);
+            for (int db = 0; db < NDA; ++db) o[db] = M::mma(vr.trans(vt, nb * 32, db, c), pp[nb][c], o[db]);
       };
       // Iteration j (par = j & 1: the loop is unrolled by two, so the register set and the stage
       // each iteration uses are static).
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
           for (int c = 0; c < M::CALLS32; ++c) settle(pc[nb][c]);
         if (need) {
 #pragma unroll
-          for (int i = 0; i < NDB; ++i)
+          for (int i = 0; i < NDA; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
         }
@@ -391,15 +406,21 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 #pragma unroll
             for (int e = (nb == nb0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
         mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
-        if (mx > m_run + kRescaleSlack) {
+        const bool need = mx > m_run + kRescaleSlack;
+        float a = 1.f;
+        if (need) {
           const float alpha = fast_exp2(m_run - mx);
 #pragma unroll
-          for (int i = 0; i < NDB; ++i)
+          for (int i = 0; i < NDA; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
           l_part *= alpha;
           m_run = mx;
+          a = alpha;
         }
+        // The 16-wide accumulators hold other lanes' queries: rescaled by all lanes together.
+        if constexpr (T16)
+          if (__ballot(need) != 0) scale_tail(a);
       };
       // Unnormalised weights 2^(s scale_log2 - m_run) of key block nb as MFMA operands, and this
       // lane's part of their row sum (bf16: the sum of the rounded weights the product uses, two
@@ -452,8 +473,15 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
 #pragma unroll
         for (int c = 0; c < M::CALLS32; ++c)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDA; ++db)
             o[db] = M::mma(vr.trans(vtile, nb * 32, db, c), pf[c], o[db]);
+        if constexpr (T16) {
+          typename M::frag lo, hi;
+          M::tail_weights(pf[0], pf[1], lo, hi);
+          const typename M::frag vt = vr.trans16(vtile, nb * 32, 32 * NDA);
+          ot[0] = M::mma16(vt, lo, ot[0]);
+          ot[1] = M::mma16(vt, hi, ot[1]);
+        }
       }
     }
     if constexpr (EARLY) {
@@ -478,16 +506,19 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   if constexpr (G == 2) {
     // Group 1 hands (m, l, O) to the wave of group 0 that owns the same queries; the tiles are no
     // longer read (the loop ended on a barrier and staged nothing after it).
-    constexpr int F = 2 + 16 * NDB;  // floats per lane
+    constexpr int F = 2 + 16 * NDA + (T16 ? 8 : 0);  // floats per lane
     static_assert(NW * 64 * F * 4 <= 2 * STG, "merge buffer fits in the tile stages");
     float* mrg = reinterpret_cast<float*>(smem) + w * F * 64 + l;
     if (grp == 1) {
       mrg[0] = m_run;
       mrg[64] = l_part;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+      for (int i = 0; i < NDA; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mrg[(2 + 16 * i + e) * 64] = o[i][e];
+      if constexpr (T16)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mrg[(2 + 16 * NDA + e) * 64] = ot[e >> 2][e & 3];
     }
     __syncthreads();
     if (grp == 1) return;
@@ -497,20 +528,38 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
     const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m);
     const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
 #pragma unroll
-    for (int i = 0; i < NDB; ++i)
+    for (int i = 0; i < NDA; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[i][e] = o[i][e] * a0 + mrg[(2 + 16 * i + e) * 64] * a1;
+    if constexpr (T16) {
+      float a0l, a0h, a1l, a1h;
+      split16(a0, a0l, a0h);
+      split16(a1, a1l, a1h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ot[0][e] = ot[0][e] * a0l + mrg[(2 + 16 * NDA + e) * 64] * a1l;
+        ot[1][e] = ot[1][e] * a0h + mrg[(2 + 16 * NDA + 4 + e) * 64] * a1h;
+      }
+    }
     l_part = l_part * a0 + l1 * a1;
     m_run = m;
   }
   const float l_tot = l_part + swap_halves(l_part);
+  // T16: lane l holds output columns d16 .. d16 + 3 of queries q16 and q16 + 16.
+  const int q16 = qw + (l & 15), d16 = 32 * NDA + 4 * (l >> 4);
   if constexpr (SPLIT) {
     // Unnormalised partial: sum_j exp2(s_j - m) v_j, with m and sum_j exp2(s_j - m) beside it.
+    const size_t prow0 = (size_t)split * BH * N + (size_t)bh * N;
+    if constexpr (T16) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        if (q16 + 16 * x < N) *reinterpret_cast<f32x4*>(part + (prow0 + q16 + 16 * x) * D + d16) = ot[x];
+    }
     if (q < N) {
-      const size_t row = (size_t)split * BH * N + (size_t)bh * N + q;
+      const size_t row = prow0 + q;
       float* prow = part + row * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDA; ++db)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int d0 = db * 32 + 8 * m + 4 * half;
@@ -531,10 +580,24 @@ __global__ __launch_bounds__(G * NW * 64, OCC) void fwd_kernel(const T* __restri
   }
   // A block-sparse mask can leave a row without keys: O = 0 and L = -inf there.
   const float inv = (BSP && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
+  if constexpr (T16) {
+    float inv2[2];
+    split16(inv, inv2[0], inv2[1]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      if (q16 + 16 * x < N) {
+        T v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = (T)(ot[x][r] * inv2[x]);
+        uint2 u;
+        __builtin_memcpy(&u, v4, 8);
+        *reinterpret_cast<uint2*>(O + (size_t)(q16 + 16 * x) * D + d16) = u;
+      }
+  }
   if (q < N) {
     T* orow = O + (size_t)q * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDA; ++db)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int d0 = db * 32 + 8 * m + 4 * half;

@@ -17,7 +17,9 @@
 //    of r mod 16.  Rows stay contiguous, so each lane's reads are one register plus an
 //    immediate offset;
 //  * skewed for transposing reads only: 128-byte rows, row r shifted by 64 (r / 4 + (r / 2) mod 2)
-//    bytes (144 bytes per row on average, as the padded pitch of such rows).
+//    bytes (144 bytes per row on average, as the padded pitch of such rows);
+//  * shifted by 16: padded rows whose rows 16-31 of every 32 are shifted by 32 bytes, for the
+//    16-column transposing reads (trans16_row), which pair rows 16 apart in one pass.
 // A tile read both as 32-row operands (16 bytes per lane) and transposed can be conflict-free for
 // both only in the skewed layout: no padded pitch is (a pitch that is an odd number of 16-byte
 // chunks suits the first, one that is 64 bytes modulo 128 the second).  Row-contiguous stores are
@@ -55,7 +57,7 @@ ATTN_HD constexpr int padded_pitch_tr(int row_bytes) {
 // (256-byte rows); padded otherwise.  (Skewed 192-byte rows for d = 80 -- the 160 data bytes and
 // 32 bytes of zero columns that pad the 32-wide operand blocks to 96 -- are defined below too; the
 // d = 80 dK/dV kernel, already at 256 registers, spills with them.)
-enum Kind { kPadded = 0, kSkewed = 1, kSkewTr = 2 };
+enum Kind { kPadded = 0, kSkewed = 1, kSkewTr = 2, kShift16 = 3 };
 ATTN_HD constexpr int kind_for(int elem_bytes, int d) {
   return elem_bytes == 2 && (d == 64 || d == 128) ? kSkewed : kPadded;
 }
@@ -85,16 +87,20 @@ ATTN_HD constexpr int skew_group_bytes(int rb) { return rb == 256 ? 4928 : rb ==
 //  * stage tiles, read both ways (dK/dV's Q and dO, dQ's K and V): skewed where kind_for says so,
 //    else padded at padded_pitch;
 //  * forward K tiles (32-row operand reads only): padded at padded_pitch;
-//  * forward V tiles (transposing reads only): kSkewTr for bfloat16 at d = 64, padded at
-//    padded_pitch_tr above d = 64, padded at padded_pitch below.
+//  * forward V tiles (transposing reads only): kSkewTr for bfloat16 at d = 64; for bfloat16 at
+//    d = 80, whose last 16 columns take the 16-column reads, kShift16 with rows at padded_pitch_tr
+//    (192 bytes: 160 of data, room for the shift); padded at padded_pitch_tr above d = 64 and at
+//    padded_pitch below.
 ATTN_HD constexpr int dp_for(int d) { return (d + 31) / 32 * 32; }
 ATTN_HD constexpr int stage_kind(int elem_bytes, int d) { return kind_for(elem_bytes, d); }
 ATTN_HD constexpr int stage_row_bytes(int elem_bytes, int d) {
   return kind_for(elem_bytes, d) != kPadded ? row_bytes_for(d) : padded_pitch(dp_for(d) * elem_bytes);
 }
-ATTN_HD constexpr int trans_kind(int elem_bytes, int d) { return elem_bytes == 2 && d == 64 ? kSkewTr : kPadded; }
+ATTN_HD constexpr int trans_kind(int elem_bytes, int d) {
+  return elem_bytes == 2 && d == 64 ? kSkewTr : elem_bytes == 2 && d == 80 ? kShift16 : kPadded;
+}
 ATTN_HD constexpr int trans_row_bytes(int elem_bytes, int d) {
-  return trans_kind(elem_bytes, d) != kPadded ? 128
+  return trans_kind(elem_bytes, d) == kSkewTr ? 128
          : dp_for(d) > 64 && elem_bytes == 2 ? padded_pitch_tr(dp_for(d) * elem_bytes)
                                              : padded_pitch(dp_for(d) * elem_bytes);
 }
@@ -103,15 +109,21 @@ ATTN_HD constexpr int trans_row_bytes(int elem_bytes, int d) {
 // 4a modulo 16, so the 4 chunks 4u .. 4u + 3 of the 4 rows fill 16 different slots: (b).
 ATTN_HD constexpr int skew_tr(int r) { return 64 * ((r >> 2) + ((r >> 1) & 1)); }
 
-// Byte offset of byte b of row r of a tile of the given layout with rows of rb bytes.
+// Byte offset of byte b of row r of a tile of the given layout with rows of rb bytes.  (kShift16:
+// a row's data plus the shift fit its rb bytes, so rows do not overlap.)
 ATTN_HD constexpr int offset(int kind, int rb, int r, int b) {
   return kind == kSkewed  ? (r >> 4) * skew_group_bytes(rb) + (r & 15) * rb + skew(rb, r) + b
          : kind == kSkewTr ? r * rb + skew_tr(r) + b
-                           : r * rb + b;
+         : kind == kShift16 ? r * rb + 32 * ((r >> 4) & 1) + b
+                            : r * rb + b;
 }
-// Byte offset of row r0 (a multiple of 16): row r0 + r, r < 16, lies at block(r0) + offset(r, b).
+// Byte offset of row r0 (a multiple of 16; of 32 for kShift16 reads that span rows r0 + 16 ..):
+// row r0 + r, r < 16, lies at block(r0) + offset(r, b).
 ATTN_HD constexpr int block(int kind, int rb, int r0) {
-  return kind == kSkewed ? (r0 >> 4) * skew_group_bytes(rb) : kind == kSkewTr ? r0 * rb + 16 * r0 : r0 * rb;
+  return kind == kSkewed    ? (r0 >> 4) * skew_group_bytes(rb)
+         : kind == kSkewTr  ? r0 * rb + 16 * r0
+         : kind == kShift16 ? r0 * rb + 32 * ((r0 >> 4) & 1)
+                            : r0 * rb;
 }
 // Bytes of a tile of `rows` rows (a multiple of 16 for the skewed layouts).
 ATTN_HD constexpr int tile_bytes(int kind, int rb, int rows) {
@@ -130,6 +142,12 @@ ATTN_HD constexpr int trans_row(int lane, int c, int h) {
   return 16 * c + 8 * h + 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
 }
 ATTN_HD constexpr int trans_byte(int lane, int col0) { return 2 * (col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)); }
+// 16-column operand of v_mfma_f32_16x16x32_bf16 (16 tile columns, reduction over the 32 rows of a
+// block): two transposing reads h = 0, 1; lane l (group g = l / 16, j = l % 16) reads the 8 bytes at
+// row 16(g % 2) + 8h + 4(g / 2) + j / 4, column col0 + 4(j % 4).  Lane group g thus walks the rows
+// that instruction c = g % 2 of the 32-column form gives to lane half g / 2.
+ATTN_HD constexpr int trans16_row(int lane, int h) { return trans_row(lane, (lane >> 4) & 1, h); }
+ATTN_HD constexpr int trans16_byte(int lane, int col0) { return 2 * (col0 + 4 * (lane & 3)); }
 // Cooperative 16-byte stores of a tile (TileCopy): chunk c = thread + i * threads goes to row
 // c / (chunks per row), byte 16 (c % chunks per row).
 ATTN_HD constexpr int store_row(int c, int chunks_per_row) { return c / chunks_per_row; }

@@ -7,6 +7,7 @@
 //   C row byte offset                                   every 16-byte chunk of every row
 //   D row0 ks a0 .. a63                                  16-byte operand read (lanes 0..63)
 //   R row0 c db h a0 .. a63                              8-byte transposing read
+//   Q row0 h a0 .. a63                                   8-byte transposing read, 16-column form
 //   S threads step wave a0 .. a63                        16-byte tile store
 // With arguments `probe FORM KIND ROW_BYTES DATA_BYTES` it prints instead the instructions of one
 // pattern of the LDS microbenchmark (P line, then D / R / S lines).
@@ -22,11 +23,13 @@ namespace {
 
 constexpr int kRows = 64;
 
-void tile(const char* name, int kind, int rb, int d, bool direct, bool trans) {
+// tail16: the last 16 columns (d = 16 modulo 32) are read with the 16-column form instead of
+// 32-column reads that reach zero columns up to dp.
+void tile(const char* name, int kind, int rb, int d, bool direct, bool trans, bool tail16 = false) {
   const int dp = dp_for(d);
   const int data = 2 * d;  // bytes of data per row (bfloat16)
   std::printf("T %s %d %d %d %d %d\n", name, kind, rb, kRows, data, tile_bytes(kind, rb, kRows));
-  const int cols = trans ? 2 * dp : data;  // the transposing reads reach the zero columns up to dp
+  const int cols = trans && !tail16 ? 2 * dp : data;  // 32-column reads reach the zero columns up to dp
   for (int r = 0; r < kRows; ++r)
     for (int b = 0; b < cols; b += 16) std::printf("C %d %d %d\n", r, b, offset(kind, rb, r, b));
   if (direct)
@@ -39,13 +42,21 @@ void tile(const char* name, int kind, int rb, int d, bool direct, bool trans) {
   if (trans)
     for (int row0 = 0; row0 < kRows; row0 += 32)
       for (int c = 0; c < 2; ++c)
-        for (int db = 0; db < dp / 32; ++db)
+        for (int db = 0; db < (tail16 ? d / 32 : dp / 32); ++db)
           for (int h = 0; h < 2; ++h) {
             std::printf("R %d %d %d %d", row0, c, db, h);
             for (int l = 0; l < 64; ++l)
               std::printf(" %d", offset(kind, rb, row0 + trans_row(l, c, h), trans_byte(l, 32 * db)));
             std::printf("\n");
           }
+  if (trans && tail16)
+    for (int row0 = 0; row0 < kRows; row0 += 32)
+      for (int h = 0; h < 2; ++h) {
+        std::printf("Q %d %d", row0, h);
+        for (int l = 0; l < 64; ++l)
+          std::printf(" %d", offset(kind, rb, row0 + trans16_row(l, h), trans16_byte(l, 32 * (d / 32))));
+        std::printf("\n");
+      }
   const int cpr = data / 16;
   for (int nt : {256, 512})
     for (int step = 0; step * nt < kRows * cpr; ++step)
@@ -108,7 +119,7 @@ int main(int argc, char** argv) {
     std::snprintf(name, sizeof name, "fwdK_d%d", d);
     tile(name, kPadded, padded_pitch(2 * dp_for(d)), d, true, false);
     std::snprintf(name, sizeof name, "fwdV_d%d", d);
-    tile(name, trans_kind(2, d), trans_row_bytes(2, d), d, false, true);
+    tile(name, trans_kind(2, d), trans_row_bytes(2, d), d, false, true, d % 32 == 16);
   }
   return 0;
 }

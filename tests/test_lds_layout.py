@@ -46,7 +46,7 @@ def _parse(text):
         f = line.split()
         if f[0] == "T":
             cur = {"kind": int(f[2]), "rb": int(f[3]), "rows": int(f[4]), "data": int(f[5]), "bytes": int(f[6]),
-                   "cells": [], "D": [], "R": [], "S": []}
+                   "cells": [], "D": [], "R": [], "S": [], "Q": []}
             tiles[f[1]] = cur
         elif f[0] == "P":
             cur = {"D": [], "R": [], "S": []}
@@ -57,6 +57,8 @@ def _parse(text):
             cur["D"].append([int(x) for x in f[3:]])
         elif f[0] == "R":
             cur["R"].append([int(x) for x in f[5:]])
+        elif f[0] == "Q":
+            cur["Q"].append([int(x) for x in f[3:]])
         elif f[0] == "S":
             cur["S"].append([int(x) for x in f[4:]])
     return tiles
@@ -104,7 +106,7 @@ def test_layouts_are_injective_and_in_bounds(tiles):
         cells = {off for _, _, off in t["cells"]}
         for a in t["D"]:
             assert all(x - x % 16 in cells for x in a), name
-        for a in t["R"]:
+        for a in t["R"] + t["Q"]:
             assert all(x - x % 16 in cells for x in a), name
         for a in t["S"]:
             assert all(x in cells for x in a if x >= 0), name
@@ -130,6 +132,19 @@ def test_transposing_reads_conflict_free(tiles, name):
     t = tiles[name]
     assert t["R"]
     assert all(trans_cycles(a) == 2 for a in t["R"]), name
+
+
+def test_sixteen_column_reads(tiles):
+    """The 16-column transposing reads of the forward's last 16 V columns at d = 80 (rows 16 apart in
+    one pass, which the kShift16 rows separate) are conflict-free; each lane's 8 bytes lie in one
+    row's data."""
+    t = tiles["fwdV_d80"]
+    assert len(t["Q"]) == 4 and len(t["R"]) == 16
+    assert all(trans_cycles(a) == 2 for a in t["Q"])
+    # with plain padded rows of the same pitch the same reads conflict 2-way
+    rb = t["rb"]
+    flat = [[(x // rb) * rb + (x % rb if (x // rb) % 32 < 16 else x % rb - 32) for x in a] for a in t["Q"]]
+    assert all(trans_cycles(a) == 4 for a in flat)
 
 
 def test_known_conflicts_d80_and_small_dims(tiles):
