@@ -131,6 +131,11 @@ __device__ __forceinline__ void dkdv_body(
   constexpr int KT = KW * NW;  // keys per workgroup
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int NDB = DP / 32;
+  // bf16 head dims of 16 modulo 32 (16, 80): the last 16 columns of dK and dV run on 16-wide
+  // products (two 16 x 16 accumulators per key block, for its keys 0-15 and 16-31); NDA full
+  // 32-row blocks precede them.
+  constexpr bool T16 = sizeof(T) == 2 && DP - D == 16;
+  constexpr int NDA = T16 ? D / 32 : NDB;
   constexpr int KS = D / M::KSTEP;
   constexpr int NQB = BQ / 32;   // query blocks per wave and stage
   constexpr int BQS = G * BQ;    // query rows per stage
@@ -171,11 +176,12 @@ __device__ __forceinline__ void dkdv_body(
   const bool wave_live = kw < kv;
   const unsigned wave_bit = 1u << ((KW * w) / kMaskBlock);  // this wave's mask column within the workgroup
 
-  f32x16 dk[KB][NDB], dv[KB][NDB];
+  f32x16 dk[KB][NDA > 0 ? NDA : 1], dv[KB][NDA > 0 ? NDA : 1];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) { dk[kb][i] = f32x16{}; dv[kb][i] = f32x16{}; }
+    for (int i = 0; i < NDA; ++i) { dk[kb][i] = f32x16{}; dv[kb][i] = f32x16{}; }
+  f32x4 dkt[KB][2] = {}, dvt[KB][2] = {};  // T16: dK^T, dV^T columns 32 NDA .. D - 1
 
   if (k0 < kv) {
     const uint32_t tbytes = (uint32_t)(N * D * sizeof(T));
@@ -207,7 +213,23 @@ __device__ __forceinline__ void dkdv_body(
           if constexpr (!VLDS) vf[kb][ks] = frag_global<T>(rv, kw + 32 * kb + col, D, ks * M::KSTEP);
         }
     }
-    const StageReader<T, D> sr;
+    const StageReader<T, D> sr(T16);
+    // T16: the 16-wide dV and dK products of one 32-query block (weights pf, dS sf as acc_frag c = 0,
+    // 1) into key block kb's tail accumulators.
+    auto tail_products = [&](int kb, const typename M::frag* pf, const typename M::frag* sf, const lds_t* qtile,
+                             const lds_t* otile, int row0) {
+      if constexpr (T16) {
+        typename M::frag lo, hi;
+        M::tail_weights(pf[0], pf[1], lo, hi);
+        const typename M::frag ot = sr.trans16(otile, row0, 32 * NDA);
+        dvt[kb][0] = M::mma16(ot, lo, dvt[kb][0]);
+        dvt[kb][1] = M::mma16(ot, hi, dvt[kb][1]);
+        M::tail_weights(sf[0], sf[1], lo, hi);
+        const typename M::frag qt = sr.trans16(qtile, row0, 32 * NDA);
+        dkt[kb][0] = M::mma16(qt, lo, dkt[kb][0]);
+        dkt[kb][1] = M::mma16(qt, hi, dkt[kb][1]);
+      }
+    };
     auto settle_kv = [&]() {
       if constexpr (STK) {
         kst.template store_to<ST>(lds + STAGE);
@@ -240,7 +262,7 @@ __device__ __forceinline__ void dkdv_body(
 
     // DSELF: D for rows [qt0*BQS, N), one row per thread at a time, kept in LDS after the stages.
     __attribute__((address_space(3))) float* dself = reinterpret_cast<__attribute__((address_space(3))) float*>(lds + 2 * STAGE);
-    if constexpr (DP > D) {
+    if constexpr (DP > D && !T16) {
       zero_pad_stage<ST, T, BQS, D, NT>(lds);
       zero_pad_stage<ST, T, BQS, D, NT>(lds + TILE);
       zero_pad_stage<ST, T, BQS, D, NT>(lds + STAGE);
@@ -399,16 +421,18 @@ __device__ __forceinline__ void dkdv_body(
               dp[qb][e] = p * dp[qb][e];
             }
           }
+          typename M::frag pf[M::CALLS32], sf[M::CALLS32];
 #pragma unroll
           for (int c = 0; c < M::CALLS32; ++c) {
-            const typename M::frag pf = M::acc_frag(s[qb], c);
-            const typename M::frag sf = M::acc_frag(dp[qb], c);
+            pf[c] = M::acc_frag(s[qb], c);
+            sf[c] = M::acc_frag(dp[qb], c);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              dv[0][db] = M::mma(sr.trans(otile, qb * 32, db, c), pf, dv[0][db]);
-              dk[0][db] = M::mma(sr.trans(qtile, qb * 32, db, c), sf, dk[0][db]);
+            for (int db = 0; db < NDA; ++db) {
+              dv[0][db] = M::mma(sr.trans(otile, qb * 32, db, c), pf[c], dv[0][db]);
+              dk[0][db] = M::mma(sr.trans(qtile, qb * 32, db, c), sf[c], dk[0][db]);
             }
           }
+          tail_products(0, pf, sf, qtile, otile, qb * 32);
         }
       } else if (run) {
 #pragma unroll
@@ -472,25 +496,27 @@ __device__ __forceinline__ void dkdv_body(
                 dp[kb][e] = p * dp[kb][e];
               }
           }
+          typename M::frag pf[KB][M::CALLS32], sf[KB][M::CALLS32];
 #pragma unroll
           for (int c = 0; c < M::CALLS32; ++c) {
-            typename M::frag pf[KB], sf[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-              pf[kb] = M::acc_frag(s[kb], c);
-              sf[kb] = M::acc_frag(dp[kb], c);
+              pf[kb][c] = M::acc_frag(s[kb], c);
+              sf[kb][c] = M::acc_frag(dp[kb], c);
             }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDA; ++db) {
               const typename M::frag ot = sr.trans(otile, qb * 32, db, c);
               const typename M::frag qt = sr.trans(qtile, qb * 32, db, c);
 #pragma unroll
               for (int kb = 0; kb < KB; ++kb) {
-                dv[kb][db] = M::mma(ot, pf[kb], dv[kb][db]);
-                dk[kb][db] = M::mma(qt, sf[kb], dk[kb][db]);
+                dv[kb][db] = M::mma(ot, pf[kb][c], dv[kb][db]);
+                dk[kb][db] = M::mma(qt, sf[kb][c], dk[kb][db]);
               }
             }
           }
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) tail_products(kb, pf[kb], sf[kb], qtile, otile, qb * 32);
         }
       }
       if constexpr (kBwdStoreEarly && D > 80) {
@@ -510,32 +536,49 @@ __device__ __forceinline__ void dkdv_body(
     // Group 1 hands its dK, dV sums to the wave of group 0 that owns the same keys (every wave of
     // the workgroup gets here; the stages are no longer read once the loop's last barrier passed).
     // 16 bytes per lane per access, consecutive lanes at consecutive addresses (conflict-free).
-    constexpr int F4 = 2 * KB * NDB * 4;  // float4s per lane
+    constexpr int F4A = 2 * KB * NDA * 4;        // float4s per lane: full blocks,
+    constexpr int F4 = F4A + (T16 ? 4 * KB : 0);  // then the 16-wide accumulators
     static_assert(NW * 64 * F4 * 16 <= 2 * STAGE, "merge buffer fits in the stages");
     f32x4* mrg = reinterpret_cast<f32x4*>(smem) + w * F4 * 64 + l;
     if (grp == 1) {
+      if constexpr (T16)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            mrg[(F4A + 4 * kb + x) * 64] = dkt[kb][x];
+            mrg[(F4A + 4 * kb + 2 + x) * 64] = dvt[kb][x];
+          }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < NDB; ++i)
+        for (int i = 0; i < NDA; ++i)
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const f32x4 k4 = {dk[kb][i][4 * m], dk[kb][i][4 * m + 1], dk[kb][i][4 * m + 2], dk[kb][i][4 * m + 3]};
             const f32x4 v4 = {dv[kb][i][4 * m], dv[kb][i][4 * m + 1], dv[kb][i][4 * m + 2], dv[kb][i][4 * m + 3]};
-            mrg[((kb * NDB + i) * 8 + m) * 64] = k4;
-            mrg[((kb * NDB + i) * 8 + 4 + m) * 64] = v4;
+            mrg[((kb * NDA + i) * 8 + m) * 64] = k4;
+            mrg[((kb * NDA + i) * 8 + 4 + m) * 64] = v4;
           }
     }
     __syncthreads();
     if (grp == 1) return;
+    if constexpr (T16)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          dkt[kb][x] += mrg[(F4A + 4 * kb + x) * 64];
+          dvt[kb][x] += mrg[(F4A + 4 * kb + 2 + x) * 64];
+        }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+      for (int i = 0; i < NDA; ++i)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const f32x4 k4 = mrg[((kb * NDB + i) * 8 + m) * 64];
-          const f32x4 v4 = mrg[((kb * NDB + i) * 8 + 4 + m) * 64];
+          const f32x4 k4 = mrg[((kb * NDA + i) * 8 + m) * 64];
+          const f32x4 v4 = mrg[((kb * NDA + i) * 8 + 4 + m) * 64];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             dk[kb][i][4 * m + r] += k4[r];
@@ -544,7 +587,21 @@ __device__ __forceinline__ void dkdv_body(
         }
   }
 
+  // T16: lane l holds columns d16 .. d16 + 3 of keys kw + 32 kb + k16 and k16 + 16.
+  const int k16 = l & 15, d16 = 32 * NDA + 4 * (l >> 4);
   if constexpr (SPLIT) {
+    if constexpr (T16)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int key = kw + 32 * kb + 16 * x + k16;
+          if (key < N) {
+            const size_t row = (size_t)split * BH * N + (size_t)bh * N + key;
+            *reinterpret_cast<f32x4*>(part + row * D + d16) = dkt[kb][x];
+            *reinterpret_cast<f32x4*>(part + (size_t)nsplit * BH * N * D + row * D + d16) = dvt[kb][x];
+          }
+        }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = kw + 32 * kb + col;
@@ -553,7 +610,7 @@ __device__ __forceinline__ void dkdv_body(
         float* prk = part + row * D;
         float* prv = part + (size_t)nsplit * BH * N * D + row * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDA; ++db)
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const int d0 = db * 32 + 8 * m + 4 * half;
@@ -572,6 +629,26 @@ __device__ __forceinline__ void dkdv_body(
     }
     return;
   }
+  if constexpr (T16)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int key = kw + 32 * kb + 16 * x + k16;
+        if (key < N) {
+          T kk[4], vv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            kk[r] = (T)(dkt[kb][x][r] * scale);
+            vv[r] = (T)dvt[kb][x][r];
+          }
+          uint2 u;
+          __builtin_memcpy(&u, kk, 8);
+          *reinterpret_cast<uint2*>(dK + (size_t)key * D + d16) = u;
+          __builtin_memcpy(&u, vv, 8);
+          *reinterpret_cast<uint2*>(dV + (size_t)key * D + d16) = u;
+        }
+      }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw + 32 * kb + col;
@@ -579,7 +656,7 @@ __device__ __forceinline__ void dkdv_body(
       T* krow = dK + (size_t)key * D;
       T* vrow = dV + (size_t)key * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDA; ++db)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int d0 = db * 32 + 8 * m + 4 * half;
@@ -657,6 +734,9 @@ __device__ __forceinline__ void dq_body(
   constexpr int QT = 32 * NW;
   constexpr int DP = (D + 31) / 32 * 32;
   constexpr int NDB = DP / 32;
+  // bf16 head dims of 16 modulo 32: dQ's last 16 columns on 16-wide products, as in dK/dV.
+  constexpr bool T16 = sizeof(T) == 2 && DP - D == 16;
+  constexpr int NDA = T16 ? D / 32 : NDB;
   constexpr int KS = D / M::KSTEP;
   constexpr int NB = BK / 32;      // key blocks per wave and tile
   constexpr int BKT = G * BK;      // keys per tile
@@ -730,11 +810,12 @@ __device__ __forceinline__ void dq_body(
     if (Oin) ocp2.load(make_rsrc(Oin + base, tbytes), q0);
   }
 
-  f32x16 acc[NDB];
+  f32x16 acc[NDA > 0 ? NDA : 1];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NDA; ++i) acc[i] = f32x16{};
+  f32x4 acct[2] = {};  // T16: dQ^T columns 32 NDA .. D - 1 of queries 0-15 and 16-31
 
-  if constexpr (DP > D) {
+  if constexpr (DP > D && !T16) {
     zero_pad_stage<ST, T, BKT, D, NT>(lds);
     zero_pad_stage<ST, T, BKT, D, NT>(lds + 2 * TILE);
   }
@@ -792,7 +873,17 @@ __device__ __forceinline__ void dq_body(
   }
   __syncthreads();
   int nxt = cur < t_hi ? after(cur) : t_hi;
-  const StageReader<T, D> sr;
+  const StageReader<T, D> sr(T16);
+  // T16: the 16-wide dQ products of one 32-key block (dS^T as acc_frag c = 0, 1).
+  auto tail_products = [&](const typename M::frag* sf, const lds_t* ktile, int row0) {
+    if constexpr (T16) {
+      typename M::frag lo, hi;
+      M::tail_weights(sf[0], sf[1], lo, hi);
+      const typename M::frag kt = sr.trans16(ktile, row0, 32 * NDA);
+      acct[0] = M::mma16(kt, lo, acct[0]);
+      acct[1] = M::mma16(kt, hi, acct[1]);
+    }
+  };
   if (nxt < t_hi) {
     kc.load(rk, nxt * BKT);
     vc.load(rv, nxt * BKT);
@@ -845,13 +936,15 @@ __device__ __forceinline__ void dq_body(
           const float p = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, -lq));
           dp[nb][e] = D > 80 ? p * dp[nb][e] : p * (dp[nb][e] - dq_);
         }
+        typename M::frag sf[M::CALLS32];
 #pragma unroll
         for (int c = 0; c < M::CALLS32; ++c) {
-          const typename M::frag sf = M::acc_frag(dp[nb], c);
+          sf[c] = M::acc_frag(dp[nb], c);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf, acc[db]);
+          for (int db = 0; db < NDA; ++db)
+            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf[c], acc[db]);
         }
+        tail_products(sf, ktile, nb * 32);
       }
     } else if (run) {
 #pragma unroll
@@ -878,13 +971,15 @@ __device__ __forceinline__ void dq_body(
           const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
           dp[e] = D > 80 ? p * dp[e] : p * (dp[e] - dq_);
         }
+        typename M::frag sf[M::CALLS32];
 #pragma unroll
         for (int c = 0; c < M::CALLS32; ++c) {
-          const typename M::frag sf = M::acc_frag(dp, c);
+          sf[c] = M::acc_frag(dp, c);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf, acc[db]);
+          for (int db = 0; db < NDA; ++db)
+            acc[db] = M::mma(sr.trans(ktile, nb * 32, db, c), sf[c], acc[db]);
         }
+        tail_products(sf, ktile, nb * 32);
       }
     }
     if constexpr (kBwdStoreEarly && D > 80) {
@@ -910,12 +1005,16 @@ __device__ __forceinline__ void dq_body(
     // Group 1 hands its dQ sums to the wave of group 0 that owns the same queries (the tiles are
     // no longer read: the loop ended on a barrier and staged nothing after it).
     // 16 bytes per lane per access, consecutive lanes at consecutive addresses (conflict-free).
-    constexpr int F4 = NDB * 4;  // float4s per lane
+    constexpr int F4 = NDA * 4 + (T16 ? 2 : 0);  // float4s per lane (the 16-wide accumulators last)
     static_assert(NW * 64 * F4 * 16 <= 4 * TILE, "merge buffer fits in the tile stages");
     f32x4* mrg = reinterpret_cast<f32x4*>(smem) + w * F4 * 64 + l;
     if (grp == 1) {
+      if constexpr (T16) {
+        mrg[(4 * NDA) * 64] = acct[0];
+        mrg[(4 * NDA + 1) * 64] = acct[1];
+      }
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+      for (int i = 0; i < NDA; ++i)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const f32x4 a4 = {acc[i][4 * m], acc[i][4 * m + 1], acc[i][4 * m + 2], acc[i][4 * m + 3]};
@@ -924,8 +1023,12 @@ __device__ __forceinline__ void dq_body(
     }
     __syncthreads();
     if (grp == 1) return;
+    if constexpr (T16) {
+      acct[0] += mrg[(4 * NDA) * 64];
+      acct[1] += mrg[(4 * NDA + 1) * 64];
+    }
 #pragma unroll
-    for (int i = 0; i < NDB; ++i)
+    for (int i = 0; i < NDA; ++i)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const f32x4 a4 = mrg[(4 * i + m) * 64];
@@ -934,11 +1037,18 @@ __device__ __forceinline__ void dq_body(
       }
   }
 
+  // T16: lane l holds columns d16 .. d16 + 3 of queries q16 and q16 + 16.
+  const int q16 = qw + (l & 15), d16 = 32 * NDA + 4 * (l >> 4);
   if constexpr (SPLIT) {
+    if constexpr (T16)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        if (q16 + 16 * x < N)
+          *reinterpret_cast<f32x4*>(part + ((size_t)split * BH * N + (size_t)bh * N + q16 + 16 * x) * D + d16) = acct[x];
     if (q < N) {
       float* prow = part + ((size_t)split * BH * N + (size_t)bh * N + q) * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDA; ++db)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int d0 = db * 32 + 8 * m + 4 * half;
@@ -952,10 +1062,21 @@ __device__ __forceinline__ void dq_body(
     }
     return;
   }
+  if constexpr (T16)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      if (q16 + 16 * x < N) {
+        T v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = (T)(acct[x][r] * scale);
+        uint2 u;
+        __builtin_memcpy(&u, v4, 8);
+        *reinterpret_cast<uint2*>(dQ + (size_t)(q16 + 16 * x) * D + d16) = u;
+      }
   if (q < N) {
     T* row = dQ + (size_t)q * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDA; ++db)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int d0 = db * 32 + 8 * m + 4 * half;

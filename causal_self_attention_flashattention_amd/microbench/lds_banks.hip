@@ -1,8 +1,8 @@
 // LDS access rates of the attention kernels' tile layouts on gfx950, one access pattern per launch.
 //
-// Each pattern is one instruction form (16-byte operand read, transposing 8-byte read pair, 16-byte
-// tile store) applied to one tile layout from lds_layout.h, with the lane addresses the kernels
-// use.  Every launch runs 256 workgroups of 8 waves; each wave issues 8 x 2048 instructions of the
+// Each pattern is one instruction form (16-byte operand read, transposing 8-byte read pair in the
+// 32- or the 16-column form, 16-byte tile store) applied to one tile layout from lds_layout.h, with
+// the lane addresses the kernels use.  Every launch runs 256 workgroups of 8 waves; each wave issues 8 x 2048 instructions of the
 // pattern against a tile of 64 rows, with all addresses computed before the timed loop.  Run it
 // under `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS GRBM_GUI_ACTIVE` to
 // see the bank-conflict cycles of each pattern (one dispatch per pattern, named by its template
@@ -28,7 +28,7 @@ constexpr int kIters = 2048;
 constexpr int kTileRows = 64;
 constexpr int kLdsBytes = 65536;
 
-enum Form { kDirect = 0, kTrans = 1, kStore = 2 };
+enum Form { kDirect = 0, kTrans = 1, kStore = 2, kTrans16 = 3 };
 
 // Byte size of a 64-row tile of the layout (kept below a third of the array: waves use 3 tiles).
 constexpr int tile_bytes(int kind, int rb) { return attn::lds::tile_bytes(kind, rb, kTileRows); }
@@ -68,6 +68,24 @@ __global__ __launch_bounds__(512) void pattern(float* out) {
       for (int r = 0; r < 8; ++r) {
         const int c = r & 1, db = (r >> 1) % NDB, blk = ((r >> 1) / NDB) & 1;
         const lds_t* p0 = tile + L::block(KIND, RB, 32 * blk + 16 * c) + 64 * db + base;
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + TR1));
+        x ^= (unsigned)(r0[0] ^ r1[3]);
+      }
+    }
+  } else if constexpr (FORM == kTrans16) {
+    // The 16-column form on the last 16 columns of the row's data (bytes DB - 32 .. DB - 1), both
+    // 32-row blocks in turn.
+    constexpr int TR1 = L::offset(KIND, RB, 8, 0) - L::offset(KIND, RB, 0, 0);
+    const int base = L::offset(KIND, RB, L::trans16_row(l, 0), L::trans16_byte(l, DB / 2 - 16));
+    for (int it = 0; it < kIters; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        // only two addresses: kept opaque so that every read is issued
+        int b = base;
+        asm volatile("" : "+v"(b));
+        const lds_t* p0 = tile + L::block(KIND, RB, 32 * (r & 1)) + b;
         const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
         const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + TR1));
         x ^= (unsigned)(r0[0] ^ r1[3]);
@@ -113,8 +131,9 @@ void run(const char* tile, float* out) {
   // bytes per instruction per wave: 1 KB (16-byte forms), 2 x 512 B (transposing pair)
   const double bytes = 8.0 * kIters * 256 * 8 * 1024;
   const double tbs = bytes / (ms * 1e-3) / 1e12;
-  static const char* forms[] = {"direct16", "trans8x2", "store16"};
-  static const char* kinds[] = {"padded", "skewed", "skew_tr"};
+  static const char* forms[] = {"direct16", "trans8x2", "store16", "trans16x2"};
+  static const char* kinds[] = {"padded", "skewed", "skew_tr", "shift16"};
+  static_assert(FORM >= 0 && FORM < 4 && KIND >= 0 && KIND < 4, "named form and layout");
   printf("%-34s %-9s %-8s row_bytes=%3d data_bytes=%3d  %7.3f ms  %6.1f B/clk/CU\n", tile, forms[FORM], kinds[KIND], RB,
          DB, ms, tbs * 1e12 / 256 / (g_ghz * 1e9));
   hipEventDestroy(e0);
@@ -138,7 +157,8 @@ int main(int argc, char** argv) {
   run<kTrans, stage_kind(2, 64), S64, 128>("stage tile d=64", out);
   run<kStore, stage_kind(2, 64), S64, 128>("stage tile d=64", out);
   run<kDirect, stage_kind(2, 80), S80, 160>("stage tile d=80", out);
-  run<kTrans, stage_kind(2, 80), S80, 192>("stage tile d=80", out);
+  run<kTrans, stage_kind(2, 80), S80, 128>("stage tile d=80", out);
+  run<kTrans16, stage_kind(2, 80), S80, 160>("stage tile d=80", out);
   run<kStore, stage_kind(2, 80), S80, 160>("stage tile d=80", out);
   // The same tiles at the padded pitch they had before (both read forms).
   run<kDirect, kPadded, padded_pitch(256), 256>("padded stage tile d=128", out);
@@ -150,7 +170,8 @@ int main(int argc, char** argv) {
   run<kDirect, kPadded, padded_pitch(128), 128>("forward K tile d=64", out);
   run<kDirect, kPadded, padded_pitch(192), 160>("forward K tile d=80", out);
   run<kTrans, trans_kind(2, 128), trans_row_bytes(2, 128), 256>("forward V tile d=128", out);
-  run<kTrans, trans_kind(2, 80), trans_row_bytes(2, 80), 192>("forward V tile d=80", out);
+  run<kTrans, trans_kind(2, 80), trans_row_bytes(2, 80), 128>("forward V tile d=80", out);
+  run<kTrans16, trans_kind(2, 80), trans_row_bytes(2, 80), 160>("forward V tile d=80", out);
   run<kTrans, trans_kind(2, 64), trans_row_bytes(2, 64), 128>("forward V tile d=64", out);
   run<kStore, trans_kind(2, 64), trans_row_bytes(2, 64), 128>("forward V tile d=64", out);
   run<kStore, trans_kind(2, 80), trans_row_bytes(2, 80), 160>("forward V tile d=80", out);
@@ -158,6 +179,7 @@ int main(int argc, char** argv) {
   run<kDirect, kPadded, 320, 256>("pitch 320", out);
   run<kTrans, kPadded, 272, 256>("pitch 272", out);
   run<kDirect, kPadded, 192, 128>("pitch 192", out);
+  run<kTrans16, kPadded, 192, 160>("pitch 192", out);
   hipFree(out);
   printf("done\n");
   return 0;

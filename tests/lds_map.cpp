@@ -92,6 +92,15 @@ void probe(int form, int kind, int rb, int db) {
                                  offset(kind, rb, trans_row(l, 0, 0), trans_byte(l, 0)) + h * tr1);
         std::printf("\n");
       }
+    } else if (form == 3) {
+      const int tr1 = offset(kind, rb, 8, 0) - offset(kind, rb, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        std::printf("Q 0 %d", h);
+        for (int l = 0; l < 64; ++l)
+          std::printf(" %d", block(kind, rb, 32 * (r & 1)) + offset(kind, rb, trans16_row(l, 0), trans16_byte(l, db / 2 - 16)) +
+                                 h * tr1);
+        std::printf("\n");
+      }
     } else {
       for (int w = 0; w < 8; ++w) {
         std::printf("S 512 %d %d", r, w);
@@ -115,7 +124,7 @@ int main(int argc, char** argv) {
   char name[64];
   for (int d : {16, 32, 64, 80, 128}) {
     std::snprintf(name, sizeof name, "stage_d%d", d);
-    tile(name, stage_kind(2, d), stage_row_bytes(2, d), d, true, true);
+    tile(name, stage_kind(2, d), stage_row_bytes(2, d), d, true, true, d % 32 == 16);
     std::snprintf(name, sizeof name, "fwdK_d%d", d);
     tile(name, kPadded, padded_pitch(2 * dp_for(d)), d, true, false);
     std::snprintf(name, sizeof name, "fwdV_d%d", d);

@@ -25,8 +25,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "causal_self_attention_flashattention_amd", "csrc")
 PROFILE = os.path.join(ROOT, "profiles", "lds_banks.txt")
 
-FORMS = {"direct16": 0, "trans8x2": 1, "store16": 2}
-KINDS = {"padded": 0, "skewed": 1, "skew_tr": 2}
+FORMS = {"direct16": 0, "trans8x2": 1, "store16": 2, "trans16x2": 3}
+KINDS = {"padded": 0, "skewed": 1, "skew_tr": 2, "shift16": 3}
 
 
 @pytest.fixture(scope="module")
@@ -49,7 +49,7 @@ def _parse(text):
                    "cells": [], "D": [], "R": [], "S": [], "Q": []}
             tiles[f[1]] = cur
         elif f[0] == "P":
-            cur = {"D": [], "R": [], "S": []}
+            cur = {"D": [], "R": [], "S": [], "Q": []}
             tiles["probe"] = cur
         elif f[0] == "C":
             cur["cells"].append((int(f[1]), int(f[2]), int(f[3])))
@@ -148,10 +148,12 @@ def test_sixteen_column_reads(tiles):
 
 
 def test_known_conflicts_d80_and_small_dims(tiles):
-    """The remaining conflicted forms, pinned as they are: the d = 80 stage tile's transposing reads
-    (padded rows: 2-way) and the stores of 160-byte rows (d = 80), which straddle the 8-lane store
-    passes."""
+    """The remaining conflicted forms, pinned as they are: the d = 80 stage tile's transposing reads,
+    32- and 16-column (padded rows: 2-way), and the stores of 160-byte rows (d = 80), which straddle
+    the 8-lane store passes."""
     assert all(trans_cycles(a) == 4 for a in tiles["stage_d80"]["R"])
+    assert len(tiles["stage_d80"]["Q"]) == 4
+    assert all(trans_cycles(a) == 4 for a in tiles["stage_d80"]["Q"])
     st = [store_cycles(a) for a in tiles["stage_d80"]["S"]]
     assert max(st) > 8
     for name in ("stage_d64", "stage_d128", "fwdK_d64", "fwdK_d128", "fwdV_d64", "fwdV_d128"):
@@ -169,7 +171,8 @@ def test_skewed_layouts_pack_tightly(tiles):
 def _profile_rows():
     rows = []
     for line in open(PROFILE):
-        m = re.match(r"(.+?)\s+(direct16|trans8x2|store16)\s+(padded|skewed|skew_tr)\s+(\d+)\s+(\d+)\s+[\d.]+\s+[\d.]+\s+"
+        m = re.match(r"(.+?)\s+(direct16|trans8x2|store16|trans16x2)\s+(padded|skewed|skew_tr|shift16)\s+(\d+)\s+(\d+)\s+"
+                     r"[\d.]+\s+[\d.]+\s+"
                      r"([\d.]+)\s+([\d.]+)\s*$", line)
         if m:
             tile, form, kind, rb, db, conf, cyc = m.groups()
@@ -191,9 +194,11 @@ def test_bank_model_matches_measured_probe_counters(lds_map):
             model = [direct_cycles(a) for a in t["D"]]
         elif form == "trans8x2":
             model = [trans_cycles(a) for a in t["R"]]
+        elif form == "trans16x2":
+            model = [trans_cycles(a) for a in t["Q"]]
         else:
             model = [store_cycles(a) for a in t["S"]]
         got = sum(model) / len(model)
         assert abs(got - cyc) <= 0.01 * cyc, (tile, form, kind, rb, db, got, cyc)
-        ideal = {"direct16": 4, "trans8x2": 2, "store16": 8}[form]
+        ideal = {"direct16": 4, "trans8x2": 2, "store16": 8, "trans16x2": 2}[form]
         assert abs((got - ideal) / got - conf) <= 0.01, (tile, form, got, conf)
