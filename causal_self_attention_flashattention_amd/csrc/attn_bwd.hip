@@ -96,6 +96,10 @@ constexpr bool kDqFull = ATTN_DQ_FULL;
 #define ATTN_DKDV_FULL 1
 #endif
 constexpr bool kDkdvFull = ATTN_DKDV_FULL;
+#ifndef ATTN_DQ_DSTEP
+#define ATTN_DQ_DSTEP 1
+#endif
+constexpr bool kDqDstep = ATTN_DQ_DSTEP;
 template <typename T, int D, int NW, int BQ, bool DSELF, bool VLDS, int KB = 1, bool BSP = false, int G = 1>
 constexpr int dkdv_lds_bytes() {
   constexpr int DP = (D + 31) / 32 * 32;
@@ -867,6 +871,21 @@ __device__ __forceinline__ void dq_body(
   }
   settle(lq);
   settle(dq_);
+  // bf16 at d = 80: -D enters the dP^T product as one more reduction step, ones (reduction rows 0
+  // and 1) against -D rounded to bf16 in two parts, hi + lo (rows 0 and 1 of this lane's query
+  // column), so that the accumulators end as dP - D with no subtraction per score.  Lanes 32-63 hold
+  // reduction rows 8-15: zero.  Measured on B=4 H=32 N=2048 d=80: 176-177 -> 172-174 us; at d = 64
+  // its 8 registers take the kernel past 128 VGPRs, from four waves per SIMD to three (+3%).
+  constexpr bool DSTEP = kDqDstep && sizeof(T) == 2 && D == 80;
+  typename M::frag ones_f{}, negd_f{};
+  if constexpr (DSTEP) {
+    if (half == 0) {
+      const __bf16 hi = (__bf16)(-dq_);
+      ones_f[0] = ones_f[1] = (__bf16)1.0f;
+      negd_f[0] = hi;
+      negd_f[1] = (__bf16)(-dq_ - (float)hi);
+    }
+  }
   if (cur < t_hi) {
     kc.template store_to<ST>(lds);
     vc.template store_to<ST>(lds + TILE);
@@ -921,6 +940,7 @@ __device__ __forceinline__ void dq_body(
         s[nb] = f32x16{};
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[nb][e] = D > 80 ? -dq_ : 0.f;
+        if constexpr (DSTEP) dp[nb] = M::mma(ones_f, negd_f, dp[nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -934,7 +954,7 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = fast_exp2(__builtin_fmaf(s[nb][e], scale_log2, -lq));
-          dp[nb][e] = D > 80 ? p * dp[nb][e] : p * (dp[nb][e] - dq_);
+          dp[nb][e] = D > 80 || DSTEP ? p * dp[nb][e] : p * (dp[nb][e] - dq_);
         }
         typename M::frag sf[M::CALLS32];
 #pragma unroll
@@ -957,6 +977,7 @@ __device__ __forceinline__ void dq_body(
         f32x16 s = f32x16{}, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[e] = D > 80 ? -dq_ : 0.f;
+        if constexpr (DSTEP) dp = M::mma(ones_f, negd_f, dp);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           s = M::mma(sr.direct(ktile, nb * 32, ks), qf[ks], s);
@@ -969,7 +990,7 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = fast_exp2(__builtin_fmaf(s[e], scale_log2, -lq));
-          dp[e] = D > 80 ? p * dp[e] : p * (dp[e] - dq_);
+          dp[e] = D > 80 || DSTEP ? p * dp[e] : p * (dp[e] - dq_);
         }
         typename M::frag sf[M::CALLS32];
 #pragma unroll
