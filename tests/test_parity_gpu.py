@@ -62,6 +62,11 @@ SMALL += [
     ("bf16", 2, 18, 1100, 128, True, [1100, 900]),
     # d = 80 with one key group per workgroup, key padding, no causal mask
     ("bf16", 2, 20, 1024, 80, False, [1000, 700]),
+    # grids small enough and chains long enough for the split paths (forward key chunks, dQ key
+    # chunks, dK/dV query chunks merged from float32 partials), whose partial writes carry the
+    # 16-wide accumulators at d = 80 (last 16 columns) and d = 16 (all columns)
+    ("bf16", 1, 2, 2048, 80, True, [1900]),
+    ("bf16", 1, 1, 2048, 16, False, None),
 ]
 
 
