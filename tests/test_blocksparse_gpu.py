@@ -52,6 +52,7 @@ CASES = [
     (2, 20, 1024, 64, "bf16", True, None, 0.3, [(0, 0), (1, 19)]),  # dQ then dK/dV launches
     (1, 128, 1024, 128, "bf16", True, None, 0.3, [(0, 5), (0, 127)]),  # 8-wave dK/dV tiles
     (1, 2, 2048, 80, "bf16", False, [1900], 0.25, None),
+    (2, 2, 300, 16, "bf16", True, [280, 300], 0.4, None),         # all of d = 16 on 16-wide products
 ]
 
 
