@@ -10,10 +10,12 @@
 //   Q row0 h a0 .. a63                                   8-byte transposing read, 16-column form
 //   S threads step wave a0 .. a63                        16-byte tile store
 // With arguments `probe FORM KIND ROW_BYTES DATA_BYTES` it prints instead the instructions of one
-// pattern of the LDS microbenchmark (P line, then D / R / S lines).
+// pattern of the LDS microbenchmark (P line, then D / R / S lines); with `rows`, the tile row each
+// lane reads in the transposing forms (W16 lane h row byte, W32 lane c h row).
 #include <cstdio>
 #include <cstdlib>
 #include <initializer_list>
+#include <string>
 
 #include "lds_layout.h"
 
@@ -117,6 +119,14 @@ void probe(int form, int kind, int rb, int db) {
 }  // namespace
 
 int main(int argc, char** argv) {
+  if (argc == 2 && std::string(argv[1]) == "rows") {  // the row maps of the transposing reads
+    for (int l = 0; l < 64; ++l)
+      for (int h = 0; h < 2; ++h) {
+        std::printf("W16 %d %d %d %d\n", l, h, trans16_row(l, h), trans16_byte(l, 0));
+        for (int c = 0; c < 2; ++c) std::printf("W32 %d %d %d %d\n", l, c, h, trans_row(l, c, h));
+      }
+    return 0;
+  }
   if (argc == 6) {  // probe FORM KIND ROW_BYTES DATA_BYTES
     probe(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]));
     return 0;
