@@ -49,6 +49,20 @@ def test_noalloc_matches_workspace_backward_twice():
             compare_all(res, oracle_ref(inp, causal, scale, heads), "bf16", heads)
 
 
+# d = 80: the split partials carry the 16-wide accumulators of the last 16 columns
+CASES80 = [(1, 2, 2048, 80, True, [1900]), (1, 1, 2048, 80, False, None)]
+
+
+def test_noalloc_matches_workspace_backward_d80():
+    require_gpu()
+    for i, (B, H, N, d, causal, kv) in enumerate(CASES80):
+        announce(f"noalloc d=80 call {i + 1}: B={B} H={H} N={N} d={d} causal={causal} kv={kv}")
+        inp, res, causal, scale = _run_pair(B, H, N, d, causal, kv, 700 + i)
+        if i == 0:
+            heads = [(0, 1)]
+            compare_all(res, oracle_ref(inp, causal, scale, heads), "bf16", heads)
+
+
 def test_noalloc_rejects_beyond_scratch():
     require_gpu()
     B, H, N, d = 1, 1, 16384, 128
