@@ -54,9 +54,8 @@ ATTN_HD constexpr int padded_pitch_tr(int row_bytes) {
 }
 
 // Layout of a bfloat16 tile read both ways: skewed rows at head dims 64 (128-byte rows) and 128
-// (256-byte rows); padded otherwise.  (Skewed 192-byte rows for d = 80 -- the 160 data bytes and
-// 32 bytes of zero columns that pad the 32-wide operand blocks to 96 -- are defined below too; the
-// d = 80 dK/dV kernel, already at 256 registers, spills with them.)
+// (256-byte rows); padded otherwise.  (Skewed 192-byte rows for d = 80 are defined below too; the
+// d = 80 backward kernels measured slower with them than with padded rows.)
 enum Kind { kPadded = 0, kSkewed = 1, kSkewTr = 2, kShift16 = 3 };
 ATTN_HD constexpr int kind_for(int elem_bytes, int d) {
   return elem_bytes == 2 && (d == 64 || d == 128) ? kSkewed : kPadded;
